@@ -1,0 +1,104 @@
+"""Pass rules for floating-point GEMM outputs (test infrastructure only).
+
+Rule (build target): an fp32 output element passes when
+    |gpu - C| <= 1e-5 * S,   S = sum_k |a_k b_k|,
+with C, S from the fp64 oracle.  A bf16 output passes when it is within one
+bf16 ulp of RNE(C), or within the fp32 rule widened by half a bf16 ulp of C.
+
+Hardware term.  The only instruction that multiplies MXFP8 operands with
+their E8M0 scales on CDNA4 (V_MFMA_SCALE_F32_*_F8F6F4) does not form an
+exact sum.  Measured on gfx950: inside each run of 8 consecutive k (aligned
+to 8) it aligns the products to the largest nominal product exponent of the
+run, emax = max(ea + eb) over the nonzero products, where ea, eb are the
+E4M3 exponents (subnormal codes count as -6) plus the scale exponents, and
+truncates every product toward zero to a multiple of 2^(emax - 13); the run
+sums are then accumulated in fp32.  A run of n nonzero products therefore
+loses less than (n - 1) * 2^(emax - 13).  The rule used by the tests is
+
+    |gpu - C| <= 1e-5 * S + H,   H = sum over runs of (n - 1) * 2^(emax - 13),
+
+and every test reports how many elements needed H (i.e. failed the strict
+1e-5 * S bound).  H is a property of the operands alone: it is computed here
+from the codes and scales, never from a GPU result.
+"""
+
+import numpy as np
+
+from . import mxfp8
+
+REL = 1e-5
+RUN = 8          # products aligned together by the MFMA
+KEEP_BITS = 13   # bits kept below the run's largest nominal exponent
+
+
+def nominal_exponents(q, s):
+    """Nominal exponent of every element of an MX tensor (blocks of 32 along
+    the last axis): E4M3 exponent (subnormal -> -6) + scale exponent.  Zero
+    codes get a very small sentinel so they never set a run's maximum."""
+    q = np.asarray(q, dtype=np.int64)
+    ef = (q >> 3) & 15
+    e = np.where(ef == 0, -6, ef - 7)
+    C = q.shape[-1]
+    sb = np.repeat(np.asarray(s, dtype=np.int64) - 127, 32, axis=-1).reshape(q.shape)
+    e = e + sb
+    return np.where((q & 0x7F) == 0, -(1 << 20), e)
+
+
+def hardware_term(ea, eb):
+    """H for element pairs: ea, eb [P, K] nominal exponents of the two
+    operand rows (sentinel for zeros).  Returns [P]."""
+    ea = np.asarray(ea, dtype=np.int64)
+    eb = np.asarray(eb, dtype=np.int64)
+    P, K = ea.shape
+    tot = ea + eb
+    nz = (ea > -(1 << 19)) & (eb > -(1 << 19))
+    tot = np.where(nz, tot, -(1 << 21)).reshape(P, K // RUN, RUN)
+    n = nz.reshape(P, K // RUN, RUN).sum(-1)
+    emax = tot.max(-1)
+    h = np.where(n > 1, (n - 1) * np.ldexp(1.0, np.maximum(emax, -1000) - KEEP_BITS), 0.0)
+    return h.sum(-1)
+
+
+def bf16_ulp(y_bits):
+    """Spacing of the bf16 grid at bf16 values y (subnormal spacing 2^-133)."""
+    y = np.abs(mxfp8.bf16_to_f64(y_bits))
+    _, x = np.frexp(y)
+    e = np.maximum(x - 1, -126)
+    return np.ldexp(1.0, e - 7)
+
+
+def check(gpu, C, S, h_fn=None, out_bf16=False):
+    """Apply the pass rule.  ``gpu``: fp32 values, or bf16 bit patterns when
+    ``out_bf16``.  ``h_fn(idx)`` returns H for the flat indices ``idx``; it is
+    only called for elements that fail the strict bound.  Returns a dict with
+    the counts and the worst ratios; ``ok`` is the verdict."""
+    C = np.asarray(C, dtype=np.float64).ravel()
+    S = np.asarray(S, dtype=np.float64).ravel()
+    if out_bf16:
+        gb = np.asarray(gpu, dtype=np.uint16).ravel()
+        g = mxfp8.bf16_to_f64(gb)
+        rc = mxfp8.f64_to_bf16(C)
+        ulp_rc = bf16_ulp(rc)
+        near = np.abs(g - mxfp8.bf16_to_f64(rc)) <= ulp_rc
+        slack = 0.5 * bf16_ulp(mxfp8.f64_to_bf16(C))
+    else:
+        g = np.asarray(gpu, dtype=np.float64).ravel()
+        near = np.zeros(C.shape, dtype=bool)
+        slack = np.zeros(C.shape)
+    err = np.abs(g - C)
+    strict = near | (err <= REL * S + slack)
+    fail_idx = np.nonzero(~strict)[0]
+    H = np.zeros(fail_idx.size)
+    if fail_idx.size and h_fn is not None:
+        H = h_fn(fail_idx)
+    final_fail = err[fail_idx] > REL * S[fail_idx] + slack[fail_idx] + H
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(S > 0, err / S, np.where(err > 0, np.inf, 0.0))
+    return {
+        "ok": bool(not final_fail.any()) and bool(np.all(np.isfinite(g))),
+        "n": int(C.size),
+        "strict_fail": int(fail_idx.size),
+        "fail": int(final_fail.sum()),
+        "max_err_over_S": float(ratio.max()) if ratio.size else 0.0,
+        "first_fail": int(fail_idx[final_fail][0]) if final_fail.any() else -1,
+    }
