@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the MXFP8 MoE expert path on one MI355X.
+
+Workload (the large expert GEMM case): 8192 tokens x hidden 5120, top-2
+routing over 16 experts (one expert forced empty) -> 16384 routed rows, ffn
+8192, bf16 inputs N(0,1) with 0.1% outliers x1000.  One step = the whole hot
+path, forward plus backward (``moe.STAGES``): X rowwise quantize, route +
+MXFP8 permute, W rowwise + columnwise quantize, grouped GEMM fwd, dY rowwise
++ columnwise quantize, grouped GEMM dgrad, X columnwise quantize in permuted
+order, grouped GEMM wgrad; GEMM outputs in bf16.  Inputs are resident in HBM
+before the timed region.
+
+Printed: one JSON line.  ``value`` = GEMM FLOPs of a step (3 x 2*M*N*K over
+the real routed rows) / step time, in TFLOP/s.  ``stages`` gives each stage's
+mean duration (HIP events on the launch stream, every timed step) and its
+throughput against the MI355X peak (MXFP8 dense 5.0 PFLOP/s, HBM 8 TB/s).
+``roofline`` reports the dominant GEMM stage.  ``quantize_bandwidth`` times
+the fused rowwise+columnwise quantize and both dequantizes of a
+[16*8192, 5120] bf16 tensor.  ``cpu_baseline`` times the oracle on a bounded
+sample (one expert's share of the step).
+"""
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MXFP8_TFLOPS = 5000.0   # MI355X dense FP8/MXFP8 MFMA
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+METRIC = "MXFP8 grouped-GEMM TFLOP/s fwd+bwd and quantize GB/s, % of MI355X peak"
+
+
+def ensure_built():
+    import mxfp8_block_scaled_07_amd as mxa
+    if not os.path.exists(mxa.LIB_PATH):
+        from mxfp8_block_scaled_07_amd import _build
+        _build.build()
+
+
+def time_stages(run, names, steps, warmup):
+    """Run ``run(name)`` for every name, ``warmup`` untimed then ``steps`` timed
+    passes; per-stage HIP events on torch's current stream (the launch stream)."""
+    import torch
+    for _ in range(warmup):
+        for n in names:
+            run(n)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        for j, n in enumerate(names):
+            ev[i][j].record()
+            run(n)
+        ev[i][-1].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j, n in enumerate(names)}
+    return total_ms / steps, per, wall
+
+
+def gpu_expert_path(args, c):
+    import numpy as np
+    import torch
+
+    from mxfp8_block_scaled_07_amd import MX_OUT_BF16, moe
+
+    T, K, N, E, topk = c["T"], c["K"], c["N"], c["E"], c["topk"]
+    dev = "cuda:0"
+    x = torch.from_numpy(c["x"].view(np.int16)).to(dev)
+    w = torch.from_numpy(c["w"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(c["expert_ids"].astype(np.int32)).to(dev)
+    dy_full = torch.from_numpy(c["dy_full"].view(np.int16)).to(dev)
+    b = moe.ExpertBuffers(T, K, N, E, topk, device=dev, out_dtype=MX_OUT_BF16)
+    moe.run_stage("quant_x", b, x, w, None, ids)
+    moe.run_stage("permute", b, x, w, None, ids)
+    dy = moe.zero_pad_rows(dy_full, b.src)
+    del dy_full
+    torch.cuda.synchronize()
+    M = T * topk
+    step_ms, per, wall = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), moe.STAGES, args.steps,
+                                     args.warmup)
+    work = moe.algorithmic_work(T, K, N, E, topk, M)
+    stages = {}
+    for n in moe.STAGES:
+        ms = per[n]
+        if n in work["gemm_flops"]:
+            tf = work["gemm_flops"][n] / (ms * 1e-3) / 1e12
+            stages[n] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4)}
+        else:
+            gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
+            stages[n] = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+    gemm_total = sum(work["gemm_flops"].values())
+    value = gemm_total / (step_ms * 1e-3) / 1e12
+    dom = max(work["gemm_flops"], key=lambda n: per[n])
+    dom_tf = work["gemm_flops"][dom] / (per[dom] * 1e-3) / 1e12
+    counts = np.bincount(c["expert_ids"].ravel(), minlength=E)
+    result = {
+        "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4), "traffic": None,
+                     "per_launch_flops": work["gemm_flops"][dom], "avg_launch_ms": round(per[dom], 4)},
+        "config": {"workload": "large expert GEMM fwd+dgrad+wgrad: T=8192 tokens, top-2 of E=16 experts "
+                               "(16384 routed rows, >=1 empty expert), hidden K=5120, ffn N=8192, "
+                               "bf16 N(0,1) inputs with 0.1% x1000 outliers, MXFP8 operands, bf16 GEMM outputs",
+                   "tokens": T, "topk": topk, "experts": E, "hidden": K, "ffn": N,
+                   "routed_rows": M, "capacity_rows": b.cap, "empty_experts": int((counts == 0).sum())},
+    }
+    del b, x, w, dy
+    torch.cuda.empty_cache()
+    return result
+
+
+def gpu_quantize_bandwidth(args):
+    import numpy as np
+    import torch
+
+    import workloads
+    import mxfp8_block_scaled_07_amd as mxa
+
+    rows, cols = 16 * 8192, 5120
+    xb = workloads.quant_tensor(4, rows, cols)
+    x = torch.from_numpy(xb.view(np.int16)).to("cuda:0")
+    del xb
+    q, s, qt, st = mxa.quantize(x, rowwise=True, colwise=True)
+    y = torch.empty_like(x)
+    yt = torch.empty((cols, rows), dtype=torch.int16, device=x.device)
+
+    def run(n):
+        if n == "quant_rowcol":
+            mxa.mx_quantize(x, 1, rows, cols, None, rows, q, s, qt, st)
+        elif n == "dequant_row":
+            mxa.mx_dequantize(q, s, rows, cols, y)
+        else:
+            mxa.mx_dequantize(qt, st, cols, rows, yt)
+
+    names = ("quant_rowcol", "dequant_row", "dequant_col")
+    _, per, _ = time_stages(run, names, max(5, args.steps // 2), 2)
+    n_el = rows * cols
+    nbytes = {"quant_rowcol": n_el * (2 + 2 * (1 + 1 / 32)), "dequant_row": n_el * (1 + 1 / 32 + 2),
+              "dequant_col": n_el * (1 + 1 / 32 + 2)}
+    out = {}
+    for n in names:
+        gbs = nbytes[n] / (per[n] * 1e-3) / 1e9
+        out[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+    out["shape"] = [rows, cols]
+    del x, q, s, qt, st, y, yt
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(args, c):
+    """The oracle, as it stands, on one expert's share of the step."""
+    import numpy as np
+
+    from oracle import gemm as og
+    from oracle import mxfp8 as mx
+    from oracle import routing
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = None
+    E = c["E"]
+    t0 = time.perf_counter()
+    counts, off, dst, src = routing.route(c["expert_ids"], E, c["capacity"])
+    e = int(np.argsort(counts)[len(counts) // 2])     # a median-sized expert
+    lo, hi = int(off[e]), int(off[e + 1])
+    rows_src = src[lo:hi]
+    xq, xs = mx.quantize_rowwise(c["x"][np.maximum(rows_src, 0)])
+    xpq, xps = routing.permute(xq, xs, np.where(rows_src >= 0, np.arange(hi - lo), -1))
+    wq, ws = mx.quantize_rowwise(c["w"][e])
+    wtq, wts = mx.quantize_colwise(c["w"][e])
+    dy = c["dy_full"][lo:hi].copy()
+    dy[rows_src < 0] = 0
+    dyq, dys = mx.quantize_rowwise(dy)
+    dytq, dyts = mx.quantize_colwise(dy)
+    xtq, xts = mx.quantize_colwise(c["x"], rows_out=hi - lo, gather=rows_src)
+    goff = np.array([0, hi - lo])
+    og.grouped_gemm_fwd(xpq, xps, wq[None], ws[None], goff, want_abs=False)
+    og.grouped_gemm_dgrad(dyq, dys, wtq[None], wts[None], goff, want_abs=False)
+    og.grouped_gemm_wgrad(dytq, dyts, xtq, xts, goff, want_abs=False)
+    dt = time.perf_counter() - t0
+    m = int(counts[e])
+    flops = 3 * 2.0 * m * c["N"] * c["K"]
+    cores = len(os.sched_getaffinity(0))
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads or cores,
+            "host_cores": cores, "kind": "oracle", "seconds": round(dt, 2),
+            "cpu": platform.processor() or platform.machine(),
+            "sample": f"one median expert ({m} routed rows of 16384): routing of all 8192x2 ids, rowwise/colwise "
+                      f"quantize of its X rows, W_e and dY rows, its permute, and fp64 fwd/dgrad/wgrad GEMMs "
+                      f"(value = its GEMM FLOPs / wall time)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quant-bench", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the expert path has no multi-GPU leg in this build "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    ensure_built()
+    import workloads
+    c = workloads.config(3)
+    res = gpu_expert_path(args, c)
+    line = {
+        "metric": METRIC, "value": round(res["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
+        "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
+    }
+    if not args.no_quant_bench:
+        line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(args, c)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * mxmoe.h -- C ABI of the MI355X (gfx950) MXFP8 Mixture-of-Experts expert path.
+ *
+ * The path: quantize bf16 activations, weights and gradients to MXFP8
+ * (rowwise and columnwise), permute tokens by expert while they stay in
+ * MXFP8, and run the block-scaled grouped GEMMs of the expert forward, dgrad
+ * and wgrad.  Sources: the engineering.fyi digest "1.5x faster MoE training
+ * on Blackwell with MXFP8 kernels built from scratch" (Overview, Key
+ * Questions Answered: microscaling and block-scaled matrix multiplies), and
+ * pytorch/ao PR #3203 (stacked-PR list: separate MXFP8 quantize and
+ * dequantize kernels, an e8m0 -> fp32 scale decode; "Next steps": an MXFP8
+ * token shuffle and a scaled grouped GEMM taking pre-quantized tensors).
+ *
+ * Format (OCP MX v1.0): blocks of 32 consecutive elements share one E8M0
+ * scale byte (value 2^(byte-127); byte 0 is 2^-127); elements are E4M3
+ * codes (bias 7, max 448, NaN = 0x7F/0xFF).  Scale exponent of a block =
+ * floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block -> byte 0);
+ * element code = round-to-nearest-even of x / 2^scale, saturating at 448.
+ *
+ * Layouts (all row-major, device memory, caller-owned):
+ *   bf16 tensors      uint16 bit patterns
+ *   rowwise MX of [R, C]      q uint8 [R, C],  s uint8 [R, C/32]
+ *   columnwise MX of [R, C]   stored transposed: q uint8 [C, R], s uint8 [C, R/32]
+ *                             (blocks are 32 consecutive rows of one column)
+ *   expert weights    W [E, N, K] (K contiguous); W^T colwise [E, K, N]
+ *   grouped rows      rows of expert e are [off[e], off[e+1]) of an M_cap-row
+ *                     buffer; off has E+1 int32 entries in device memory.
+ *
+ * Conventions:
+ *   - Every call validates its host-side arguments first and returns a
+ *     status (MX_OK or a negative MX_E* code) without touching the GPU when
+ *     they are invalid.  Valid calls enqueue kernels on `stream` (a
+ *     hipStream_t; NULL = the default stream) and return without waiting;
+ *     MX_EHIP reports a launch failure.
+ *   - The library allocates nothing and keeps no global state; all buffers
+ *     are passed in.  Calls are thread-safe; calls on one stream are ordered.
+ *   - Device-side contents are trusted for meaning but never for memory
+ *     safety: out-of-range expert ids are ignored, group offsets are clamped
+ *     to [0, M_cap] and made monotone before use.
+ */
+#ifndef MXMOE_H
+#define MXMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* mx_stream_t; /* a hipStream_t */
+
+enum {
+  MX_OK = 0,
+  MX_EINVAL = -1,       /* a null pointer, a bad size or alignment, a bad dtype */
+  MX_EUNSUPPORTED = -2, /* a valid request this build does not implement */
+  MX_EHIP = -3          /* the HIP runtime reported an error at launch */
+};
+
+enum { MX_OUT_BF16 = 0, MX_OUT_F32 = 1 };
+
+/* Human-readable name of a status code (static storage). */
+const char* mx_status_string(int status);
+
+/*
+ * MXFP8 quantize (digest "Key Questions Answered": a scale per fine-grained
+ * sub-block; PR #3203 stacked list: MXFP8 quantization kernel).
+ *
+ *   x        bf16 [batch, rows, cols]
+ *   gather   optional int32 [rows_out] (batch must be 1): output row r is
+ *            source row gather[r], or an all-zero row when gather[r] < 0;
+ *            entries >= rows also give zero rows.  Without a gather, output
+ *            row r is source row r for r < rows and zero after.
+ *   rows_out rows of the quantized output (per batch item)
+ *   row_q/row_s  rowwise result [batch, rows_out, cols] / [batch, rows_out, cols/32],
+ *            or both NULL to skip it
+ *   col_q/col_s  columnwise result stored transposed [batch, cols, rows_out] /
+ *            [batch, cols, rows_out/32], or both NULL to skip it
+ * One kernel reads x once and writes every requested output.  Requires
+ * cols % 32 == 0; rows_out % 32 == 0 when a columnwise output is asked for;
+ * at least one output.  Expert groups laid out at multiples of 32 with zero
+ * pad rows (as mx_permute's src_row gives) never share a columnwise block.
+ */
+int mx_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* gather,
+                int64_t rows_out, uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, uint8_t* col_s,
+                mx_stream_t stream);
+
+/*
+ * MXFP8 dequantize (PR #3203 stacked list: MXFP8 dequantization kernel and
+ * the e8m0 -> fp32 scale decode).  y = RNE_bf16(decode(q) * 2^(s-127)),
+ * bf16 subnormals kept, overflow to Inf, NaN codes or scale 255 -> NaN.
+ *   q uint8 [rows, cols], s uint8 [rows, cols/32] (blocks along cols),
+ *   y bf16 [rows, cols].  A columnwise tensor is dequantized as the
+ *   [cols, rows] matrix it is stored as.  Requires cols % 32 == 0.
+ */
+int mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, uint16_t* y,
+                  mx_stream_t stream);
+
+/* Bytes of device workspace mx_permute needs for these sizes. */
+size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts);
+
+/*
+ * MXFP8 token permute (PR #3203 "Next steps": a token shuffle that stays in
+ * MXFP8; TransformerEngine issue #556, first maintainer reply: fp8 data
+ * moves as bytes as long as its scales move with it).
+ *
+ *   q, s          rowwise MX tokens [tokens, cols] / [tokens, cols/32]
+ *                 (both NULL, with q_out/s_out NULL: metadata only)
+ *   expert_ids    int32 [tokens, topk]; flat pair i = t*topk + j
+ *   capacity_rows rows of the permuted buffers, >= tokens*topk + 31*num_experts
+ *   q_out, s_out  [capacity_rows, cols] / [capacity_rows, cols/32]
+ *   group_offsets int32 [num_experts+1]: expert e owns rows [off[e], off[e+1]);
+ *                 every group is padded to a multiple of 32 rows
+ *   dst_row       int32 [tokens*topk]: permuted row of pair i (-1 if its id
+ *                 is out of range)
+ *   src_row       int32 [capacity_rows]: source token of each permuted row,
+ *                 -1 for pad rows and rows past the last group
+ *   workspace     >= mx_permute_workspace_size(...) bytes of device memory
+ * Rows of one expert keep the order of their flat pair index (stable), so
+ * the result is deterministic.  Pad rows get codes 0x00 and scales 0x00.
+ */
+int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
+               int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,
+               int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
+               size_t workspace_bytes, mx_stream_t stream);
+
+/*
+ * Block-scaled grouped GEMMs (digest "Key Questions Answered": block-scaled
+ * MMA; PR #3203 "Next steps": grouped GEMM on pre-quantized tensors).  All
+ * three are C[m, n] = sum_k A[m, k] B[n, k] with both operands contiguous
+ * along k and the E8M0 scales applied inside the CDNA4 scaled MFMA;
+ * accumulation in fp32.  out_dtype is MX_OUT_BF16 (RNE) or MX_OUT_F32.
+ * Sizes: n % 32 == 0, k % 32 == 0, m_cap >= 0, num_groups >= 1.
+ *
+ * fwd:   a = X_perm rowwise [m_cap, k], b = W rowwise [E, n, k],
+ *        out Y [m_cap, n].  Rows of group e multiply W_e; rows outside every
+ *        group are not written.
+ * dgrad: a = dY rowwise [m_cap, n_c], b = W^T colwise [E, k_o, n_c]
+ *        (same call shape as fwd with n = k_o, k = n_c), out dX [m_cap, k_o].
+ * wgrad: a = dY^T colwise [n, m_cap], b = X^T colwise [k, m_cap],
+ *        out dW [E, n, k]; group e contracts over columns
+ *        [off[e], off[e+1]) (multiples of 32, m_cap % 32 == 0); an empty
+ *        group writes an exact zero dW_e.
+ */
+int mx_grouped_gemm_fwd(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
+                        const int32_t* group_offsets, int32_t num_groups, int64_t m_cap, int64_t n, int64_t k,
+                        void* out, int32_t out_dtype, mx_stream_t stream);
+
+int mx_grouped_gemm_dgrad(const uint8_t* dy_q, const uint8_t* dy_s, const uint8_t* wt_q, const uint8_t* wt_s,
+                          const int32_t* group_offsets, int32_t num_groups, int64_t m_cap, int64_t n_out,
+                          int64_t k_contract, void* dx, int32_t out_dtype, mx_stream_t stream);
+
+int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s, const uint8_t* xt_q, const uint8_t* xt_s,
+                          const int32_t* group_offsets, int32_t num_groups, int64_t m_cap, int64_t n, int64_t k,
+                          void* dw, int32_t out_dtype, mx_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXMOE_H */

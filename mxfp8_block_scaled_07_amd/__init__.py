@@ -1,0 +1,153 @@
+"""MI355X (gfx950) MXFP8 Mixture-of-Experts expert path.
+
+Python binding of ``libmxmoe.so`` (declared in ``include/mxmoe.h``).  The
+functions named ``mx_*`` mirror the C entry points one to one and only
+marshal arguments: torch tensors stand for device buffers (their data
+pointers are passed), ``None`` stands for NULL, and the stream defaults to
+torch's current stream.  The ``alloc_*``/convenience helpers only allocate
+output tensors with torch and then call the same entry points.  Every
+computation runs in the HIP kernels; there is no fallback: if the library is
+missing or a call fails, an exception is raised.
+"""
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
+
+MX_OK, MX_EINVAL, MX_EUNSUPPORTED, MX_EHIP = 0, -1, -2, -3
+MX_OUT_BF16, MX_OUT_F32 = 0, 1
+
+_lib = None
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_SIGNATURES = {
+    "mx_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mx_quantize": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "mx_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "mx_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
+    "mx_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mx_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "mx_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "mx_grouped_gemm_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+}
+
+
+class MXError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MXError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = h
+    return _lib
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _s(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(rc, name):
+    if rc != MX_OK:
+        raise MXError(f"{name}: {lib().mx_status_string(rc).decode()}")
+
+
+# --- entry points (same names and argument order as include/mxmoe.h) -------
+def mx_quantize(x, batch, rows, cols, gather, rows_out, row_q, row_s, col_q, col_s, stream=None):
+    _check(lib().mx_quantize(_p(x), batch, rows, cols, _p(gather), rows_out, _p(row_q), _p(row_s), _p(col_q),
+                             _p(col_s), _s(stream)), "mx_quantize")
+
+
+def mx_dequantize(q, s, rows, cols, y, stream=None):
+    _check(lib().mx_dequantize(_p(q), _p(s), rows, cols, _p(y), _s(stream)), "mx_dequantize")
+
+
+def mx_permute_workspace_size(tokens, topk, num_experts):
+    return int(lib().mx_permute_workspace_size(tokens, topk, num_experts))
+
+
+def mx_permute(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out, group_offsets,
+               dst_row, src_row, workspace, workspace_bytes, stream=None):
+    _check(lib().mx_permute(_p(q), _p(s), tokens, cols, _p(expert_ids), topk, num_experts, capacity_rows, _p(q_out),
+                            _p(s_out), _p(group_offsets), _p(dst_row), _p(src_row), _p(workspace), workspace_bytes,
+                            _s(stream)), "mx_permute")
+
+
+def mx_grouped_gemm_fwd(a_q, a_s, b_q, b_s, group_offsets, num_groups, m_cap, n, k, out, out_dtype, stream=None):
+    _check(lib().mx_grouped_gemm_fwd(_p(a_q), _p(a_s), _p(b_q), _p(b_s), _p(group_offsets), num_groups, m_cap, n, k,
+                                     _p(out), out_dtype, _s(stream)), "mx_grouped_gemm_fwd")
+
+
+def mx_grouped_gemm_dgrad(dy_q, dy_s, wt_q, wt_s, group_offsets, num_groups, m_cap, n_out, k_contract, dx,
+                          out_dtype, stream=None):
+    _check(lib().mx_grouped_gemm_dgrad(_p(dy_q), _p(dy_s), _p(wt_q), _p(wt_s), _p(group_offsets), num_groups, m_cap,
+                                       n_out, k_contract, _p(dx), out_dtype, _s(stream)), "mx_grouped_gemm_dgrad")
+
+
+def mx_grouped_gemm_wgrad(dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m_cap, n, k, dw, out_dtype,
+                          stream=None):
+    _check(lib().mx_grouped_gemm_wgrad(_p(dyt_q), _p(dyt_s), _p(xt_q), _p(xt_s), _p(group_offsets), num_groups, m_cap,
+                                       n, k, _p(dw), out_dtype, _s(stream)), "mx_grouped_gemm_wgrad")
+
+
+# --- allocating helpers ----------------------------------------------------
+def quantize(x, rowwise=True, colwise=False, rows_out=None, gather=None, stream=None):
+    """x: bf16 (or int16 bit) tensor [rows, cols] or [batch, rows, cols] on the GPU.
+    Returns (row_q, row_s, col_q, col_s); unrequested outputs are None."""
+    import torch
+    if x.dim() == 2:
+        batch, rows, cols = 1, x.shape[0], x.shape[1]
+    else:
+        batch, rows, cols = x.shape
+    rows_out = rows if rows_out is None else rows_out
+    dev = x.device
+    shp = (rows_out, cols) if x.dim() == 2 else (batch, rows_out, cols)
+    row_q = torch.empty(shp, dtype=torch.uint8, device=dev) if rowwise else None
+    row_s = torch.empty(shp[:-1] + (cols // 32,), dtype=torch.uint8, device=dev) if rowwise else None
+    cshp = (cols, rows_out) if x.dim() == 2 else (batch, cols, rows_out)
+    col_q = torch.empty(cshp, dtype=torch.uint8, device=dev) if colwise else None
+    col_s = torch.empty(cshp[:-1] + (rows_out // 32,), dtype=torch.uint8, device=dev) if colwise else None
+    mx_quantize(x, batch, rows, cols, gather, rows_out, row_q, row_s, col_q, col_s, stream)
+    return row_q, row_s, col_q, col_s
+
+
+def dequantize(q, s, stream=None):
+    import torch
+    y = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    mx_dequantize(q, s, q.shape[-2] if q.dim() > 1 else 1, q.shape[-1], y, stream)
+    return y
+
+
+def permute(q, s, expert_ids, num_experts, capacity_rows=None, stream=None):
+    """Returns (q_out, s_out, group_offsets, dst_row, src_row); q/s may be None
+    (metadata only)."""
+    import torch
+    tokens, topk = expert_ids.shape
+    dev = expert_ids.device
+    cap = -(-(tokens * topk + 31 * num_experts) // 32) * 32 if capacity_rows is None else capacity_rows
+    cols = q.shape[1] if q is not None else 0
+    q_out = torch.empty((cap, cols), dtype=torch.uint8, device=dev) if q is not None else None
+    s_out = torch.empty((cap, cols // 32), dtype=torch.uint8, device=dev) if q is not None else None
+    off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    dst = torch.empty(tokens * topk, dtype=torch.int32, device=dev)
+    src = torch.empty(cap, dtype=torch.int32, device=dev)
+    wsb = mx_permute_workspace_size(tokens, topk, num_experts)
+    ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
+    mx_permute(q, s, tokens, cols, expert_ids, topk, num_experts, cap, q_out, s_out, off, dst, src, ws, wsb, stream)
+    return q_out, s_out, off, dst, src

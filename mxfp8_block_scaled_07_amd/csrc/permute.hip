@@ -1,0 +1,184 @@
+// Routing metadata and the MXFP8 token permute (gfx950).
+//
+// pytorch/ao PR #3203, "Next steps": shuffle tokens by expert while they stay
+// in MXFP8 so no dequantize is needed before the grouped GEMM.
+// NVIDIA/TransformerEngine issue #556, first maintainer reply: fp8 data moves
+// as plain bytes as long as the scales move with them -- the copy below moves
+// each token's E4M3 codes and E8M0 scales together, untouched.
+//
+// Deterministic, stable ranks without ordering atomics:
+//   1. k_route_hist   per tile of kTile flat pairs, an expert histogram
+//   2. k_route_scan   counts, padded exclusive scan -> group_offsets, and the
+//                     first row of every (tile, expert)
+//   3. k_route_rank   one wave per tile walks its pairs in flat order; a pair's
+//                     row is its tile base + the number of earlier pairs of the
+//                     same expert (wave ballots give the in-chunk part)
+//   4. k_permute_rows copies q/s rows (pad rows -> zeros), 16 B per lane.
+
+#include "mx_device.h"
+
+namespace mx {
+namespace {
+
+constexpr int kTile = 4096;  // flat (token, slot) pairs per routing tile
+
+__global__ void __launch_bounds__(256) k_route_hist(const int32_t* __restrict__ ids, int64_t n, int32_t E,
+                                                    int32_t* __restrict__ hist) {
+  extern __shared__ int32_t lh[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) lh[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kTile;
+  for (int i = threadIdx.x; i < kTile; i += blockDim.x) {
+    const int64_t f = base + i;
+    if (f < n) {
+      const int32_t e = ids[f];
+      if (e >= 0 && e < E) atomicAdd(&lh[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = lh[e];
+}
+
+// One block; thread e owns expert e (loops when E > blockDim).
+__global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__ hist, int32_t ntiles, int32_t E,
+                                                     int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+  extern __shared__ int32_t padded[];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t c = 0;
+    for (int t = 0; t < ntiles; ++t) c += hist[(int64_t)t * E + e];
+    padded[e] = (c + 31) & ~31;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {  // E is small (experts): a serial scan is plenty
+    int32_t acc = 0;
+    for (int e = 0; e < E; ++e) {
+      const int32_t p = padded[e];
+      padded[e] = acc;
+      offsets[e] = acc;
+      acc += p;
+    }
+    offsets[E] = acc;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int32_t acc = padded[e];
+    for (int t = 0; t < ntiles; ++t) {
+      base[(int64_t)t * E + e] = acc;
+      acc += hist[(int64_t)t * E + e];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) k_fill_i32(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// One wave (64 lanes) per tile.
+__global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ ids, int64_t n, int32_t topk, int32_t E,
+                                                   const int32_t* __restrict__ base, int32_t* __restrict__ dst_row,
+                                                   int32_t* __restrict__ src_row, int64_t capacity) {
+  extern __shared__ int32_t next_row[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < E; e += 64) next_row[e] = base[(int64_t)blockIdx.x * E + e];
+  __syncthreads();
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t t0 = (int64_t)blockIdx.x * kTile;
+  for (int c = 0; c < kTile; c += 64) {
+    const int64_t f = t0 + c + lane;
+    int32_t e = -1;
+    if (f < n) e = ids[f];
+    const bool valid = (e >= 0 && e < E);
+    // lanes holding the same (valid) expert id
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const uint64_t ones = __ballot(valid && ((e >> b) & 1));
+      peers &= ((e >> b) & 1) ? ones : ~ones;
+    }
+    int32_t row = -1;
+    if (valid) row = next_row[e] + __popcll(peers & lt_mask);
+    __syncthreads();
+    if (valid) {
+      // the last lane of each expert's peer group advances the cursor
+      const uint64_t gt = peers & ~lt_mask & ~(1ull << lane);
+      if (gt == 0) next_row[e] += __popcll(peers);
+    }
+    __syncthreads();
+    if (f < n) {
+      dst_row[f] = row;
+      if (row >= 0 && row < capacity) src_row[row] = (int32_t)(f / topk);
+    }
+  }
+}
+
+// One wave per output row; 4 rows per block.  Rows copy codes then scales.
+__global__ void __launch_bounds__(256) k_permute_rows(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                      int64_t tokens, int64_t cols, const int32_t* __restrict__ src_row,
+                                                      int64_t capacity, uint8_t* __restrict__ q_out,
+                                                      uint8_t* __restrict__ s_out) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= capacity) return;
+  const int32_t src = src_row[r];
+  const bool ok = src >= 0 && src < tokens;
+  const int64_t nq = cols >> 4;  // 16-B chunks of codes (cols % 32 == 0)
+  const uint4* qs = reinterpret_cast<const uint4*>(q + (ok ? src : 0) * cols);
+  uint4* qd = reinterpret_cast<uint4*>(q_out + r * cols);
+  for (int64_t i = lane; i < nq; i += 64) qd[i] = ok ? qs[i] : make_uint4(0, 0, 0, 0);
+  const int64_t ns = cols >> 5;  // scale bytes
+  const uint8_t* ss = s + (ok ? src : 0) * ns;
+  uint8_t* sd = s_out + r * ns;
+  for (int64_t i = lane; i < ns; i += 64) sd[i] = ok ? ss[i] : (uint8_t)0;
+}
+
+}  // namespace
+}  // namespace mx
+
+using namespace mx;
+
+static int64_t route_tiles(int64_t n) { return (n + kTile - 1) / kTile; }
+
+extern "C" size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts) {
+  if (tokens < 0 || topk < 1 || num_experts < 1) return 0;
+  const int64_t nt = route_tiles(tokens * topk);
+  return (size_t)(2 * (nt > 0 ? nt : 1) * num_experts) * sizeof(int32_t);
+}
+
+extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
+                          int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,
+                          int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
+                          size_t workspace_bytes, mx_stream_t stream) {
+  const bool copy = q || s || q_out || s_out;
+  if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > 65536) return MX_EINVAL;
+  if (!group_offsets || !src_row || (tokens > 0 && (!expert_ids || !dst_row))) return MX_EINVAL;
+  if (copy && (!q || !s || !q_out || !s_out || cols <= 0 || cols % 32)) return MX_EINVAL;
+  const int64_t n = tokens * topk;
+  if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
+  if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t nt = route_tiles(n) > 0 ? route_tiles(n) : 1;
+  if (nt > 0x7FFFFFFF) return MX_EINVAL;
+  int32_t* hist = static_cast<int32_t*>(workspace);
+  int32_t* base = hist + nt * num_experts;
+  const size_t lds = (size_t)num_experts * sizeof(int32_t);
+  if (lds > 64 * 1024) return MX_EINVAL;
+  if (n > 0) {
+    hipLaunchKernelGGL(k_route_hist, dim3((unsigned)route_tiles(n)), dim3(256), lds, st, expert_ids, n, num_experts,
+                       hist);
+  } else {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, hist, (int64_t)num_experts, 0);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), lds, st, hist, (int32_t)(n > 0 ? route_tiles(n) : 1),
+                     num_experts, base, group_offsets);
+  const int64_t fill_blocks = (capacity_rows + 255) / 256 < 65536 ? (capacity_rows + 255) / 256 : 65536;
+  if (capacity_rows > 0)
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)fill_blocks), dim3(256), 0, st, src_row, capacity_rows, -1);
+  if (n > 0)
+    hipLaunchKernelGGL(k_route_rank, dim3((unsigned)route_tiles(n)), dim3(64), lds, st, expert_ids, n, topk,
+                       num_experts, base, dst_row, src_row, capacity_rows);
+  if (copy && capacity_rows > 0)
+    hipLaunchKernelGGL(k_permute_rows, dim3((unsigned)((capacity_rows + 3) / 4)), dim3(256), 0, st, q, s, tokens,
+                       cols, src_row, capacity_rows, q_out, s_out);
+  return launch_status();
+}

@@ -1,0 +1,94 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/mxmoe.h declares, and rejects invalid host-side arguments with the
+documented status codes before touching the GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp8_block_scaled_07_amd as mxa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "mxmoe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mxa.LIB_PATH):
+        from mxfp8_block_scaled_07_amd import _build
+        _build.build()
+    return mxa.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"mx_quantize", "mx_dequantize", "mx_permute", "mx_permute_workspace_size",
+                          "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
+                          "mx_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.mx_status_string(0) == b"MX_OK"
+    assert lib.mx_status_string(-1).startswith(b"MX_EINVAL")
+    assert lib.mx_status_string(-3).startswith(b"MX_EHIP")
+
+
+P = ctypes.c_void_p(16)  # a non-null dummy pointer: never dereferenced on these paths
+
+
+def test_quantize_validation(lib):
+    q = lib.mx_quantize
+    assert q(None, 1, 32, 32, None, 32, P, P, None, None, None) == mxa.MX_EINVAL          # x null
+    assert q(P, 1, 32, 48, None, 32, P, P, None, None, None) == mxa.MX_EINVAL             # cols % 32
+    assert q(P, 1, 32, 32, None, 32, None, None, None, None, None) == mxa.MX_EINVAL       # no output
+    assert q(P, 1, 32, 32, None, 32, P, None, None, None, None) == mxa.MX_EINVAL          # half a pair
+    assert q(P, 1, 32, 32, None, 40, None, None, P, P, None) == mxa.MX_EINVAL             # colwise rows_out % 32
+    assert q(P, 2, 32, 32, P, 32, P, P, None, None, None) == mxa.MX_EINVAL                # gather with batch
+    assert q(P, 1, 32, 32, None, 0, P, P, None, None, None) == mxa.MX_OK                  # empty: no launch
+
+
+def test_dequantize_validation(lib):
+    d = lib.mx_dequantize
+    assert d(None, P, 4, 32, P, None) == mxa.MX_EINVAL
+    assert d(P, P, 4, 33, P, None) == mxa.MX_EINVAL
+    assert d(P, P, 0, 32, P, None) == mxa.MX_OK
+
+
+def test_permute_validation(lib):
+    ws = lib.mx_permute_workspace_size(100, 2, 4)
+    assert ws >= 2 * 4 * 4
+    p = lib.mx_permute
+    # capacity below tokens*topk + 31*E
+    assert p(P, P, 100, 64, P, 2, 4, 200 + 31 * 4 - 1, P, P, P, P, P, P, ws, None) == mxa.MX_EINVAL
+    # workspace too small
+    assert p(P, P, 100, 64, P, 2, 4, 400, P, P, P, P, P, P, ws - 1, None) == mxa.MX_EINVAL
+    # copy requested with a missing output
+    assert p(P, P, 100, 64, P, 2, 4, 400, None, P, P, P, P, P, ws, None) == mxa.MX_EINVAL
+    assert p(None, None, 100, 0, P, 0, 4, 400, None, None, P, P, P, P, ws, None) == mxa.MX_EINVAL   # topk 0
+
+
+def test_gemm_validation(lib):
+    for fn in (lib.mx_grouped_gemm_fwd, lib.mx_grouped_gemm_dgrad):
+        assert fn(P, P, P, P, P, 2, 64, 48, 64, P, 0, None) == mxa.MX_EINVAL   # n % 32
+        assert fn(P, P, P, P, P, 2, 64, 64, 40, P, 0, None) == mxa.MX_EINVAL   # k % 32
+        assert fn(P, P, P, P, P, 0, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL   # no groups
+        assert fn(P, P, P, P, P, 2, 64, 64, 64, P, 7, None) == mxa.MX_EINVAL   # dtype
+        assert fn(P, P, None, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL
+        assert fn(P, P, P, P, P, 2, 0, 64, 64, P, 0, None) == mxa.MX_OK        # no rows: nothing to do
+    w = lib.mx_grouped_gemm_wgrad
+    assert w(P, P, P, P, P, 2, 48, 64, 64, P, 0, None) == mxa.MX_EINVAL        # m_cap % 32
+    assert w(P, P, P, P, None, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL
+
+
+def test_python_binding_raises(lib):
+    with pytest.raises(mxa.MXError):
+        mxa.mx_dequantize(None, None, 4, 32, None, stream=0)

@@ -1,0 +1,87 @@
+"""GPU parity: routing metadata and the MXFP8 token permute vs the oracle,
+bit-exact (pytorch/ao PR #3203 "Next steps": token shuffle in MXFP8;
+TransformerEngine issue #556: codes move together with their scales)."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp8_block_scaled_07_amd as mxa
+import workloads
+from oracle import mxfp8 as mx
+from oracle import routing
+
+from gpu_util import dev, host
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def check_permute(ids, E, K=64, seed=0, copy=True, cap=None):
+    ids = np.asarray(ids, np.int32).reshape(len(ids), -1)
+    T, topk = ids.shape
+    cap = T * topk + 31 * E if cap is None else cap
+    g = np.random.default_rng(seed)
+    xb = workloads.normal_bf16(g, (T, K))
+    q, s = mx.quantize_rowwise(xb)
+    counts, off, dst, src = routing.route(ids, E, cap)
+    qd = dev(q) if copy else None
+    sd = dev(s) if copy else None
+    q_out, s_out, goff, gdst, gsrc = mxa.permute(qd, sd, dev(ids), E, cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(goff), off)
+    assert np.array_equal(host(gdst), dst)
+    assert np.array_equal(host(gsrc), src)
+    if copy:
+        oq, os_ = routing.permute(q, s, src)
+        assert np.array_equal(host(q_out), oq) and np.array_equal(host(s_out), os_)
+    return host(gsrc)
+
+
+def test_golden_route():
+    with open(os.path.join(GOLDEN, "route_small.json")) as fh:
+        gd = json.load(fh)
+    check_permute(gd["expert_ids"], gd["num_experts"])
+
+
+def test_workload3_routing_full_width():
+    """8192 tokens, top-2 of 16 experts with one empty expert, 5120 columns."""
+    c = workloads.moe_case(3, 8192, 32, 32, 16, 2, empty_experts=[5], with_dy=False)
+    ids = c["expert_ids"]
+    assert not np.any(ids == 5)
+    check_permute(ids, 16, K=5120, seed=3)
+
+
+def test_top8_of_64_routing():
+    c = workloads.moe_case(5, 32768, 32, 32, 64, 8, with_dy=False)
+    check_permute(c["expert_ids"], 64, K=256, seed=5)
+
+
+@pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 3, 2), (63, 2, 7), (4097, 1, 3), (3000, 2, 300), (100, 4, 1)])
+def test_edge_shapes(T, topk, E):
+    g = np.random.default_rng(T * 7 + E)
+    ids = g.integers(0, E, (T, topk))
+    check_permute(ids, E, K=32 * int(g.integers(1, 4)), seed=T)
+
+
+def test_all_tokens_one_expert_and_duplicates():
+    ids = np.zeros((300, 2), np.int32)
+    ids[::3, 1] = 2
+    check_permute(ids, 4)
+
+
+def test_metadata_only_and_extra_capacity():
+    g = np.random.default_rng(2)
+    ids = g.integers(0, 6, (500, 2))
+    check_permute(ids, 6, copy=False)
+    check_permute(ids, 6, cap=500 * 2 + 31 * 6 + 77)
+
+
+def test_permute_deterministic():
+    c = workloads.moe_case(3, 8192, 32, 32, 16, 2, with_dy=False)
+    a = check_permute(c["expert_ids"], 16, K=128)
+    b = check_permute(c["expert_ids"], 16, K=128)
+    assert np.array_equal(a, b)

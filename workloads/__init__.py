@@ -58,8 +58,10 @@ def normal_bf16(g, shape, std=1.0, outlier_p=0.0, outlier_g=None):
 
 
 def capacity(T, topk, E):
-    """Rows a padded permuted buffer needs in the worst case."""
-    return T * topk + (BLOCK - 1) * E
+    """Rows of a padded permuted buffer: the worst case T*topk + 31*E rounded
+    up to a multiple of 32 (columnwise blocks run along these rows)."""
+    n = T * topk + (BLOCK - 1) * E
+    return -(-n // BLOCK) * BLOCK
 
 
 def ids_from_sizes(sizes):
