@@ -28,10 +28,10 @@
 // trip); a load past a row or contraction bound returns zeros, which pads
 // ragged tiles for free.  Two LDS stages (2 x 66 KB): the loads of step s+1
 // fly while step s computes.  LDS rows are 128 B with the 16-byte chunks
-// XOR-swizzled by row so the 16 rows read by a lane group hit distinct banks.
-// Tiles are ordered so that the tiles running at the same time on one XCD
-// (blocks are dealt round-robin over the 8 XCDs) share operand rows in that
-// XCD's L2.
+// XOR-swizzled by row so fragment reads are free of bank conflicts.
+// Workgroups are persistent (one per CU) and walk the output tiles of their
+// XCD's share in an order where concurrently running tiles share operand rows
+// in that XCD's L2.
 
 #include "mx_device.h"
 
@@ -47,9 +47,16 @@ constexpr int kThreads = 256;
 constexpr int kTileBytes = BM * BK;                          // one operand, one stage
 constexpr int kStageBytes = 2 * kTileBytes + 2 * BM * 4;     // A, B, A scales, B scales
 constexpr int kXcds = 8;
+constexpr int kMaxGroups = 2048;                            // experts per grouped GEMM call
 constexpr uint32_t kOob = 0x80000000u;                       // voffset that reads as zero
 
-__device__ __forceinline__ int swz(int r) { return (r + (r >> 3)) & 7; }
+// 16-byte chunk swizzle of LDS row r.  ds_read_b128 serves 8 lanes (128 B)
+// at a time; the 8 rows read by one such group must hit 8 distinct chunk
+// columns.  Measured on gfx950: this XOR keeps fragment reads at the full
+// LDS rate (~240 B/clk/CU), where (r + r/8) & 7 reaches only ~150.  It
+// depends on r mod 16 only, so all fragments a lane reads share one chunk
+// column and differ by a constant (immediate) offset.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // One operand tile: rows [0, rows) of a matrix starting at the tile's first
 // row, ld bytes per row, scales ld/32 bytes per row.
@@ -71,21 +78,23 @@ __device__ __forceinline__ TileSrc make_src(const uint8_t* q, const uint8_t* s, 
   return t;
 }
 
-// Codes of one operand tile, k window [k0, k0+128) with valid k in [k_lo, k_hi).
-// Wave w fills 8 LDS blocks of 1 KB (8 rows each); lane l writes slot l.
-__device__ __forceinline__ void load_codes(const TileSrc& t, uint8_t* lds_tile, int64_t k0, int64_t k_lo, int64_t k_hi) {
+// Codes of one operand tile, k window [k0, k0+128) with valid k in [k_lo, k_hi):
+// block i (of 8) of wave w, i.e. LDS block 8w+i of 1 KB (8 rows); lane l
+// writes slot l.
+__device__ __forceinline__ void load_codes_blk(const TileSrc& t, uint8_t* lds_tile, int64_t k0, int64_t k_lo,
+                                               int64_t k_hi, int i) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int blk = 8 * w + i;
-    const int row = 8 * blk + (lane >> 3);
-    const int c = (lane & 7) ^ swz(row);
-    const int64_t k = k0 + 16 * c;
-    const bool ok = row < t.rows && k >= k_lo && k < k_hi;
-    const uint32_t voff = ok ? (uint32_t)(row * t.ld + k) : kOob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(t.q, (lds_void*)(lds_tile + blk * 1024), 16, voff, 0, 0, 0);
-  }
+  const int blk = 8 * w + i;
+  const int row = 8 * blk + (lane >> 3);
+  const int c = (lane & 7) ^ swz(row);
+  // branch-free, 32-bit (tile spans are below 2^31): a lane-dependent branch
+  // here would split the step into divergent blocks and stop the scheduler
+  // from interleaving the loads with the MFMAs
+  const int32_t k = (int32_t)k0 + 16 * c;
+  const bool ok = (row < t.rows) & (k >= (int32_t)k_lo) & (k < (int32_t)k_hi);
+  const uint32_t voff = ok ? (uint32_t)row * (uint32_t)t.ld + (uint32_t)k : kOob;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(t.q, (lds_void*)(lds_tile + blk * 1024), 16, voff, 0, 0, 0);
 }
 
 // The 4 scale bytes of the k step for each of the tile's 256 rows -> one
@@ -94,22 +103,21 @@ __device__ __forceinline__ void load_scales_direct(const TileSrc& t, uint8_t* ld
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = 64 * w + lane;
-  const uint32_t voff = row < t.rows ? (uint32_t)(row * (t.ld >> 5) + (k0 >> 5)) : kOob;
+  const uint32_t voff = row < t.rows ? (uint32_t)row * (uint32_t)(t.ld >> 5) + (uint32_t)(k0 >> 5) : kOob;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(t.s, (lds_void*)(lds_sc + w * 256), 4, voff, 0, 0, 0);
 }
 
-// Byte path (ld not a multiple of 128): gather the 4 bytes into a register.
+// Byte path (ld not a multiple of 128): gather the 4 bytes into a register
+// (branch free: a byte outside the row reads as zero).
 __device__ __forceinline__ uint32_t load_scales_bytes(const TileSrc& t, int64_t k0) {
   const int row = threadIdx.x;
+  const int32_t nb = (int32_t)(t.ld >> 5);
   uint32_t v = 0;
-  if (row < t.rows) {
-    const int64_t nb = t.ld >> 5;
-    const uint8_t* p = t.sp + row * nb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t b = (k0 >> 5) + j;
-      if (b >= 0 && b < nb) v |= (uint32_t)p[b] << (8 * j);
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int32_t b = (int32_t)(k0 >> 5) + j;
+    const uint32_t voff = ((row < t.rows) & (b < nb)) ? (uint32_t)row * (uint32_t)nb + (uint32_t)b : kOob;
+    v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(t.s, voff, 0, 0) << (8 * j);
   }
   return v;
 }
@@ -122,74 +130,6 @@ __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
-}
-
-// 64 MFMAs: acc[i][j] (A rows 16i.., B rows 16j.. of the wave's 128 x 128).
-__device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], int wm, int wn) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const uint8_t* At = st;
-  const uint8_t* Bt = st + kTileBytes;
-  const uint32_t* Sa = reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes);
-  const uint32_t* Sb = Sa + BM;
-  v8i bf[8];
-  int sb[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rb = wn * 128 + 16 * j + r;
-    bf[j] = frag(Bt, rb, g);
-    sb[j] = (int)(Sb[rb] >> (8 * g));
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ra = wm * 128 + 16 * i + r;
-    const v8i af = frag(At, ra, g);
-    const int sa = (int)(Sa[ra] >> (8 * g));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af, acc[i][j], 0, 0, 0, sb[j], 0, sa);
-  }
-}
-
-// Accumulate C over k in [k_lo, k_hi); k steps start at k_begin (a multiple of 128).
-template <bool kScaleDirect>
-__device__ __forceinline__ void mainloop(uint8_t* smem, const TileSrc& A, const TileSrc& B, int64_t k_begin,
-                                         int64_t k_lo, int64_t k_hi, v4f (&acc)[8][8], int wm, int wn) {
-  if (k_hi <= k_lo) return;
-  const int steps = (int)((k_hi - k_begin + BK - 1) / BK);
-  auto issue = [&](int stage, int64_t k0, uint32_t& sa_reg, uint32_t& sb_reg) {
-    uint8_t* st = smem + stage * kStageBytes;
-    load_codes(A, st, k0, k_lo, k_hi);
-    load_codes(B, st + kTileBytes, k0, k_lo, k_hi);
-    if (kScaleDirect) {
-      load_scales_direct(A, st + 2 * kTileBytes, k0);
-      load_scales_direct(B, st + 2 * kTileBytes + BM * 4, k0);
-    } else {
-      sa_reg = load_scales_bytes(A, k0);
-      sb_reg = load_scales_bytes(B, k0);
-    }
-  };
-  auto park = [&](int stage, uint32_t sa_reg, uint32_t sb_reg) {
-    if (!kScaleDirect) {
-      uint32_t* sc = reinterpret_cast<uint32_t*>(smem + stage * kStageBytes + 2 * kTileBytes);
-      sc[threadIdx.x] = sa_reg;
-      sc[BM + threadIdx.x] = sb_reg;
-    }
-  };
-  uint32_t sa_reg = 0, sb_reg = 0;
-  issue(0, k_begin, sa_reg, sb_reg);
-  park(0, sa_reg, sb_reg);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int s = 0; s < steps; ++s) {
-    const bool more = s + 1 < steps;
-    if (more) issue((s + 1) & 1, k_begin + (int64_t)(s + 1) * BK, sa_reg, sb_reg);
-    mma_step(smem + (s & 1) * kStageBytes, acc, wm, wn);
-    if (more) park((s + 1) & 1, sa_reg, sb_reg);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  }
 }
 
 // Rows [m0, m0 + rows) x cols [n0, n_end) of an output with ldc elements per row.
@@ -210,91 +150,122 @@ __device__ __forceinline__ void store_tile(void* out, int64_t ldc, int64_t m0, i
       if (kF32) {
         *reinterpret_cast<float4*>(static_cast<float*>(out) + m * ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
-        const uint2 p = make_uint2(f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16));
+        const uint2 p = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
         *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + m * ldc + n) = p;
       }
     }
   }
 }
 
-__device__ __forceinline__ int64_t clamp_off(const int32_t* off, int e, int64_t limit) {
-  const int64_t v = off[e];
-  return v < 0 ? 0 : (v > limit ? limit : v);
+// One output tile's work: operand sources, contraction window, destination.
+struct Tile {
+  TileSrc A, B;
+  int64_t k_begin, k_lo, k_hi;  // k steps start at k_begin; valid k in [k_lo, k_hi)
+  int steps;
+  void* out;
+  int64_t ldc, m0, n0, n_end;
+};
+
+// Group schedule shared by the workgroup: clamped, monotone group bounds and
+// (row-grouped problems) the running count of tiles before each group.
+struct Sched {
+  int32_t bound[kMaxGroups + 1];
+  int32_t tiles_before[kMaxGroups + 1];
+};
+
+// Inclusive wave scan (sum or max) over the 64 lanes.
+template <bool kMax>
+__device__ __forceinline__ int32_t wave_scan(int32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v = kMax ? (o > v ? o : v) : v + o;
+  }
+  return v;
 }
 
-// Block -> logical tile: blocks are dealt round-robin over the XCDs, so give
-// each XCD a contiguous range of logical tiles.  Returns -1 for idle blocks.
-__device__ __forceinline__ int64_t logical_tile(int64_t total) {
-  const int64_t per = (total + kXcds - 1) / kXcds;
-  const int64_t x = blockIdx.x % kXcds, s = blockIdx.x / kXcds;
-  if (s >= per) return -1;
-  const int64_t L = x * per + s;
-  return L < total ? L : -1;
-}
-
-// fwd / dgrad: rows grouped.  Within a group tiles run n-tile major, m-tile
-// minor, so the m tiles of a group (a few) reuse each B tile back to back.
-template <bool kF32, bool kScaleDirect>
-__global__ void __launch_bounds__(kThreads) k_gemm_rows(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
-                                                        const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
-                                                        const int32_t* __restrict__ offsets, int32_t E, int64_t m_cap,
-                                                        int64_t N, int64_t K, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
-  const int64_t n_tiles = (N + BN - 1) / BN;
-  int64_t total = 0;
-  {
-    int64_t lo = clamp_off(offsets, 0, m_cap);
-    for (int g = 0; g < E; ++g) {
-      int64_t hi = clamp_off(offsets, g + 1, m_cap);
-      hi = hi < lo ? lo : hi;
-      total += (hi - lo + BM - 1) / BM * n_tiles;
-      lo = hi;
+// Wave 0 builds the schedule for E groups; tiles per group = ceil(len / BM) * n_tiles
+// (n_tiles = 0 skips the tile counts).
+__device__ void build_schedule(Sched& sc, const int32_t* offsets, int E, int64_t m_cap, int32_t n_tiles, bool align32) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int32_t carry_max = 0, carry_sum = 0, prev_last = 0;
+    for (int base = 0; base <= E; base += 64) {
+      const int i = base + lane;
+      int32_t v = 0;
+      if (i <= E) {
+        const int64_t o = offsets[i];
+        v = (int32_t)(o < 0 ? 0 : (o > m_cap ? m_cap : o));
+        if (align32) v &= ~31;
+      }
+      v = wave_scan<true>(v);
+      v = v > carry_max ? v : carry_max;
+      if (i <= E) sc.bound[i] = v;
+      // tiles of group i-1 = [bound[i-1], bound[i])
+      const int32_t left = __shfl_up(v, 1, 64);
+      const int32_t lo = lane == 0 ? prev_last : left;
+      int32_t t = 0;
+      if (i >= 1 && i <= E && n_tiles > 0) t = (v - lo + BM - 1) / BM * n_tiles;
+      int32_t ps = wave_scan<false>(t) + carry_sum;
+      if (i <= E) sc.tiles_before[i] = ps;
+      carry_max = __shfl(v, 63, 64);
+      carry_sum = __shfl(ps, 63, 64);
+      prev_last = carry_max;
     }
   }
-  const int64_t L = logical_tile(total);
-  if (L < 0) return;
-  int64_t lo = clamp_off(offsets, 0, m_cap), base = 0;
-  int e = 0;
-  int64_t hi = lo, mt_e = 0;
-  for (; e < E; ++e) {
-    hi = clamp_off(offsets, e + 1, m_cap);
-    hi = hi < lo ? lo : hi;
-    mt_e = (hi - lo + BM - 1) / BM;
-    if (L < base + mt_e * n_tiles) break;
-    base += mt_e * n_tiles;
-    lo = hi;
+  __syncthreads();
+}
+
+// Schedule entries are the same for every lane: read them into scalar registers.
+__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Largest e in [0, E) with tiles_before[e] <= L (skips groups without tiles).
+__device__ __forceinline__ int find_group(const Sched& sc, int E, int64_t L) {
+  int lo = 0, hi = E;  // tiles_before[lo] <= L < tiles_before[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (uni(sc.tiles_before[mid]) <= L) lo = mid; else hi = mid;
   }
-  const int64_t rem = L - base;
+  return lo;
+}
+
+struct RowsProblem {
+  const uint8_t *a_q, *a_s, *b_q, *b_s;
+  int64_t m_cap, N, K;
+  void* out;
+  bool f32;
+};
+
+__device__ __forceinline__ Tile rows_tile(const RowsProblem& p, const Sched& sc, int E, int64_t n_tiles, int64_t L) {
+  Tile t;
+  const int e = find_group(sc, E, L);
+  const int64_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);
+  const int64_t mt_e = (hi - lo + BM - 1) / BM;
+  const int64_t rem = L - uni(sc.tiles_before[e]);
   const int64_t nt = rem / mt_e;
   const int64_t mt = rem - nt * mt_e;
   const int64_t row0 = lo + mt * BM;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  v4f acc[8][8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  const TileSrc A = make_src(a_q, a_s, K, row0, hi - row0);
-  const TileSrc B = make_src(b_q + (int64_t)e * N * K, b_s + (int64_t)e * N * (K >> 5), K, nt * BN, N - nt * BN);
-  mainloop<kScaleDirect>(smem, A, B, 0, 0, K, acc, wm, wn);
-  store_tile<kF32>(out, N, row0, A.rows, nt * BN, N, acc, wm, wn);
+  t.A = make_src(p.a_q, p.a_s, p.K, row0, hi - row0);
+  t.B = make_src(p.b_q + (int64_t)e * p.N * p.K, p.b_s + (int64_t)e * p.N * (p.K >> 5), p.K, nt * BN, p.N - nt * BN);
+  t.k_begin = 0;
+  t.k_lo = 0;
+  t.k_hi = p.K;
+  t.steps = (int)((p.K + BK - 1) / BK);
+  t.out = p.out;
+  t.ldc = p.N;
+  t.m0 = row0;
+  t.n0 = nt * BN;
+  t.n_end = p.N;
+  return t;
 }
 
-// wgrad: contraction grouped.  Within an expert, tiles are walked in bands of
-// 4 m tiles (n-tile major inside a band) so concurrent tiles share A and B.
-template <bool kF32, bool kScaleDirect>
-__global__ void __launch_bounds__(kThreads) k_gemm_wgrad(const uint8_t* __restrict__ a_q, const uint8_t* __restrict__ a_s,
-                                                         const uint8_t* __restrict__ b_q, const uint8_t* __restrict__ b_s,
-                                                         const int32_t* __restrict__ offsets, int32_t E, int64_t m_cap,
-                                                         int64_t N, int64_t K, void* __restrict__ out) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
-  const int64_t m_tiles = (N + BM - 1) / BM;
-  const int64_t n_tiles = (K + BN - 1) / BN;
+// wgrad: tiles of an expert walked in bands of 4 m tiles, n-tile major inside
+// a band, so concurrently running tiles share A and B rows.
+__device__ __forceinline__ Tile wgrad_tile(const RowsProblem& p, const Sched& sc, int64_t m_tiles, int64_t n_tiles,
+                                           int64_t L) {
+  Tile t;
   const int64_t per = m_tiles * n_tiles;
-  const int64_t L = logical_tile((int64_t)E * per);
-  if (L < 0) return;
   const int64_t e = L / per;
   const int64_t rem = L - e * per;
   constexpr int64_t kBand = 4;
@@ -304,45 +275,258 @@ __global__ void __launch_bounds__(kThreads) k_gemm_wgrad(const uint8_t* __restri
   const int64_t in_band = rem - band * kBand * n_tiles;
   const int64_t mt = first_m + in_band % band_m;
   const int64_t nt = in_band / band_m;
-  // group e contracts over [lo, hi): clamped, monotone, whole 32-blocks
-  int64_t lo = 0;
-  for (int g = 0; g <= e; ++g) {
-    const int64_t v = clamp_off(offsets, g, m_cap);
-    lo = v > lo ? v : lo;
+  const int64_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);  // whole 32-blocks
+  // here p.N is the dW row count and p.K its column count; the contraction runs over m_cap
+  t.A = make_src(p.a_q, p.a_s, p.m_cap, mt * BM, p.N - mt * BM);
+  t.B = make_src(p.b_q, p.b_s, p.m_cap, nt * BN, p.K - nt * BN);
+  t.k_begin = lo & ~(int64_t)(BK - 1);
+  t.k_lo = lo;
+  t.k_hi = hi;
+  t.steps = hi > lo ? (int)((hi - t.k_begin + BK - 1) / BK) : 0;
+  t.out = p.f32 ? (void*)(static_cast<float*>(p.out) + e * p.N * p.K) : (void*)(static_cast<uint16_t*>(p.out) + e * p.N * p.K);
+  t.ldc = p.K;
+  t.m0 = mt * BM;
+  t.n0 = nt * BN;
+  t.n_end = p.K;
+  return t;
+}
+
+// The loads of one k stage (A and B codes plus scales) into LDS stage dst,
+// issued in 8 parts so they can be spread between MFMAs.
+struct StageLoad {
+  TileSrc A, B;
+  uint8_t* dst;
+  int64_t k0, k_lo, k_hi;
+  bool active;
+};
+
+template <bool kScaleDirect>
+__device__ __forceinline__ void issue_part(const StageLoad& sl, int i, uint32_t& sa_reg, uint32_t& sb_reg) {
+  load_codes_blk(sl.A, sl.dst, sl.k0, sl.k_lo, sl.k_hi, i);
+  load_codes_blk(sl.B, sl.dst + kTileBytes, sl.k0, sl.k_lo, sl.k_hi, i);
+  if (i == 0) {
+    if (kScaleDirect) {
+      load_scales_direct(sl.A, sl.dst + 2 * kTileBytes, sl.k0);
+      load_scales_direct(sl.B, sl.dst + 2 * kTileBytes + BM * 4, sl.k0);
+    } else {
+      sa_reg = load_scales_bytes(sl.A, sl.k0);
+      sb_reg = load_scales_bytes(sl.B, sl.k0);
+    }
   }
-  int64_t hi = clamp_off(offsets, (int)e + 1, m_cap);
-  lo &= ~(int64_t)31;
-  hi &= ~(int64_t)31;
-  hi = hi < lo ? lo : hi;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-  v4f acc[8][8];
+}
+
+template <bool kScaleDirect>
+__device__ __forceinline__ void issue_stage(const StageLoad& sl, uint32_t& sa_reg, uint32_t& sb_reg) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) issue_part<kScaleDirect>(sl, i, sa_reg, sb_reg);
+}
+
+// One k step of the wave's 128 x 128 sub-tile: 64 MFMAs, acc[i][j] covering
+// A rows 16i.. and B rows 16j...  All 8 B fragments stay in registers; the A
+// fragments are double buffered so row i+1 is read while row i multiplies.
+// The next stage's loads are issued two at a time between the MFMA rows:
+// issued back to back they stall the wave for thousands of cycles (memory
+// pipeline back-pressure) before the first MFMA.
+template <bool kScaleDirect>
+__device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], int wm, int wn, const StageLoad& sl,
+                                         uint32_t& sa_reg, uint32_t& sb_reg) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int g = lane >> 4;
+  const uint8_t* At = st;
+  const uint8_t* Bt = st + kTileBytes;
+  const uint32_t* Sa = reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes);
+  const uint32_t* Sb = Sa + BM;
+  v8i bf[8], af[2];
+  int sb[8], sa[2];
+  af[0] = frag(At, wm * 128 + r, g);
+  sa[0] = (int)(Sa[wm * 128 + r] >> (8 * g));
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int rb = wn * 128 + 16 * j + r;
+    bf[j] = frag(Bt, rb, g);
+    sb[j] = (int)(Sb[rb] >> (8 * g));
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    issue_part<kScaleDirect>(sl, i, sa_reg, sb_reg);
+    if (i < 7) {
+      const int ra = wm * 128 + 16 * (i + 1) + r;
+      af[(i + 1) & 1] = frag(At, ra, g);
+      sa[(i + 1) & 1] = (int)(Sa[ra] >> (8 * g));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], acc[i][j], 0, 0, 0, sb[j], 0,
+                                                                   sa[i & 1]);
+  }
+  // Instruction order for the machine scheduler (the MFMA builtins are pure
+  // and would otherwise all sink below the loads): the fragment reads first,
+  // then per row: its share of the next stage's loads, the next A fragment,
+  // and the row's 8 MFMAs.
+#define MX_ROW(nvmem, nds)                                                   \
+  __builtin_amdgcn_sched_group_barrier(0x020, nvmem, 0); /* VMEM read */     \
+  __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   /* DS read */       \
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     /* MFMA */
+  __builtin_amdgcn_sched_group_barrier(0x100, 27, 0);  // A0, its scale, 8 B fragments and their scales
+  MX_ROW(kScaleDirect ? 4 : 10, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 3)
+  MX_ROW(2, 0)
+#undef MX_ROW
+  __builtin_amdgcn_sched_barrier(0);
+  // The MFMA results are only consumed steps later, so the compiler would sink
+  // the whole step's MFMAs below the step's s_waitcnt / s_barrier and they
+  // would stop hiding the load latency.  An empty asm that claims to update
+  // the accumulators keeps them above it.
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                 "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+}
+
+template <bool kScaleDirect>
+__device__ __forceinline__ void park_scales(uint8_t* st, uint32_t sa_reg, uint32_t sb_reg) {
+  if (!kScaleDirect) {
+    uint32_t* sc = reinterpret_cast<uint32_t*>(st + 2 * kTileBytes);
+    sc[threadIdx.x] = sa_reg;
+    sc[BM + threadIdx.x] = sb_reg;
+  }
+}
+
+__device__ __forceinline__ void zero_acc(v4f (&acc)[8][8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  const TileSrc A = make_src(a_q, a_s, m_cap, mt * BM, N - mt * BM);
-  const TileSrc B = make_src(b_q, b_s, m_cap, nt * BN, K - nt * BN);
-  mainloop<kScaleDirect>(smem, A, B, lo & ~(int64_t)(BK - 1), lo, hi, acc, wm, wn);
-  void* dst = kF32 ? (void*)(static_cast<float*>(out) + e * N * K) : (void*)(static_cast<uint16_t*>(out) + e * N * K);
-  store_tile<kF32>(dst, K, mt * BM, A.rows, nt * BN, K, acc, wm, wn);
 }
 
-template <bool kF32, bool kDirect>
-void launch_rows(dim3 grid, hipStream_t st, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
-                 const uint8_t* b_s, const int32_t* off, int32_t E, int64_t m_cap, int64_t N, int64_t K, void* out) {
-  hipLaunchKernelGGL((k_gemm_rows<kF32, kDirect>), grid, dim3(kThreads), 0, st, a_q, a_s, b_q, b_s, off, E, m_cap, N,
-                     K, out);
+// Tile source of the persistent loop (row-grouped or wgrad problems).
+template <bool kWgrad>
+struct TileGen {
+  const RowsProblem& p;
+  const Sched& sc;
+  int E;
+  int64_t m_tiles, n_tiles;
+  __device__ __forceinline__ Tile operator()(int64_t l) const {
+    return kWgrad ? wgrad_tile(p, sc, m_tiles, n_tiles, l) : rows_tile(p, sc, E, n_tiles, l);
+  }
+};
+
+// One k step: MFMAs on LDS stage CUR while the next stage (the next k window
+// of this tile, or the first one of the next tile) streams into the other.
+// The two stages are distinct LDS objects and each step names them
+// statically, so the compiler sees that the reads of one never alias the
+// in-flight DMA writes of the other and does not wait for those loads
+// before reading.
+template <int CUR, bool kScaleDirect, typename Gen>
+__device__ __forceinline__ void k_step(uint8_t* st0, uint8_t* st1, const Tile& cur, int s, bool has_next, int64_t Ln,
+                                       const Gen& gen, bool& staged, v4f (&acc)[8][8], int wm, int wn) {
+  uint8_t* comp = CUR ? st1 : st0;
+  uint8_t* pre = CUR ? st0 : st1;
+  __builtin_amdgcn_sched_barrier(0);  // keep each step's fragment reads inside the step
+  uint32_t sa_reg = 0, sb_reg = 0;
+  StageLoad sl{cur.A, cur.B, pre, cur.k_begin + (int64_t)(s + 1) * BK, cur.k_lo, cur.k_hi, s + 1 < cur.steps};
+  if (!sl.active && has_next) {
+    const Tile nxt = gen(Ln);
+    if (nxt.steps > 0) {
+      sl = StageLoad{nxt.A, nxt.B, pre, nxt.k_begin, nxt.k_lo, nxt.k_hi, true};
+      staged = true;
+    }
+  }
+  if (!sl.active) {  // nothing to prefetch: every load of the stage becomes a zero read
+    sl.A.rows = sl.B.rows = 0;
+    sl.k_hi = sl.k_lo;
+  }
+  mma_step<kScaleDirect>(comp, acc, wm, wn, sl, sa_reg, sb_reg);
+  if (sl.active) park_scales<kScaleDirect>(pre, sa_reg, sb_reg);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool kF32, bool kDirect>
-void launch_wgrad(dim3 grid, hipStream_t st, const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
-                  const uint8_t* b_s, const int32_t* off, int32_t E, int64_t m_cap, int64_t N, int64_t K, void* out) {
-  hipLaunchKernelGGL((k_gemm_wgrad<kF32, kDirect>), grid, dim3(kThreads), 0, st, a_q, a_s, b_q, b_s, off, E, m_cap,
-                     N, K, out);
+// Persistent workgroup: one per CU.  Logical tiles are split into 8 contiguous
+// ranges, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an
+// XCD walk their range round robin.  The first k stage of the next tile is
+// loaded during the last k step of the current one, so tile changes cost no
+// exposed load latency and the epilogue stores overlap the next loads.
+template <bool kF32, bool kScaleDirect, bool kWgrad>
+__global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t* __restrict__ offsets, int32_t E) {
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
+  __shared__ Sched sc;
+  const int64_t m_tiles = (p.N + BM - 1) / BM;  // wgrad only
+  const int64_t n_tiles = kWgrad ? (p.K + BN - 1) / BN : (p.N + BN - 1) / BN;
+  build_schedule(sc, offsets, E, p.m_cap, kWgrad ? 0 : (int32_t)n_tiles, kWgrad);
+  const int64_t total = kWgrad ? (int64_t)E * m_tiles * n_tiles : (int64_t)uni(sc.tiles_before[E]);
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  const int64_t ctas_per_xcd = gridDim.x / kXcds;
+  const int64_t x = blockIdx.x % kXcds;
+  const int64_t L_end = (x + 1) * per_xcd < total ? (x + 1) * per_xcd : total;
+  int64_t L = x * per_xcd + blockIdx.x / kXcds;
+  if (L >= L_end) return;
+  const TileGen<kWgrad> gen{p, sc, E, m_tiles, n_tiles};
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  v4f acc[8][8];
+  zero_acc(acc);
+  Tile cur = gen(L);
+  int buf = 0;  // stage holding the current tile's first k window
+  bool staged = false;
+  while (true) {
+    if (cur.steps > 0 && !staged) {
+      uint32_t sa_reg = 0, sb_reg = 0;
+      uint8_t* st = buf ? st1 : st0;
+      const StageLoad sl{cur.A, cur.B, st, cur.k_begin, cur.k_lo, cur.k_hi, true};
+      issue_stage<kScaleDirect>(sl, sa_reg, sb_reg);
+      park_scales<kScaleDirect>(st, sa_reg, sb_reg);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int64_t Ln = L + ctas_per_xcd;
+    const bool has_next = Ln < L_end;
+    staged = false;
+    int s = 0;
+    if (buf && s < cur.steps) k_step<1, kScaleDirect>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
+    while (s + 1 < cur.steps) {
+      k_step<0, kScaleDirect>(st0, st1, cur, s, has_next, Ln, gen, staged, acc, wm, wn);
+      k_step<1, kScaleDirect>(st0, st1, cur, s + 1, has_next, Ln, gen, staged, acc, wm, wn);
+      s += 2;
+    }
+    if (s < cur.steps) k_step<0, kScaleDirect>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
+    buf = (buf + cur.steps) & 1;
+    store_tile<kF32>(cur.out, cur.ldc, cur.m0, cur.A.rows, cur.n0, cur.n_end, acc, wm, wn);
+    zero_acc(acc);
+    if (!has_next) break;
+    cur = gen(Ln);
+    L = Ln;
+  }
 }
 
-int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+template <bool kF32, bool kDirect, bool kWgrad>
+void launch(int ctas, hipStream_t st, const RowsProblem& p, const int32_t* off, int32_t E) {
+  hipLaunchKernelGGL((k_gemm<kF32, kDirect, kWgrad>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
+}
+
+template <bool kWgrad>
+int launch_any(const RowsProblem& p, bool direct, const int32_t* off, int32_t E, hipStream_t st) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MX_EHIP;
+  const int ctas = (cus > 0 ? (cus + kXcds - 1) / kXcds : 1) * kXcds;
+  if (p.f32) {
+    if (direct) launch<true, true, kWgrad>(ctas, st, p, off, E);
+    else launch<true, false, kWgrad>(ctas, st, p, off, E);
+  } else {
+    if (direct) launch<false, true, kWgrad>(ctas, st, p, off, E);
+    else launch<false, false, kWgrad>(ctas, st, p, off, E);
+  }
+  return launch_status();
+}
 
 }  // namespace
 }  // namespace mx
@@ -355,22 +539,12 @@ static int gemm_rows(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
   if (!a_q || !a_s || !b_q || !b_s || !offsets || !out) return MX_EINVAL;
   if (E < 1 || m_cap < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
-  if ((int64_t)BM * K >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile
+  if ((int64_t)BM * K >= (1ll << 31) || m_cap >= (1ll << 31)) return MX_EINVAL;  // 32-bit tile spans and bounds
+  if (E > kMaxGroups) return MX_EUNSUPPORTED;
   if (m_cap == 0) return MX_OK;
-  const int64_t n_tiles = (N + BN - 1) / BN;
-  const int64_t blocks = round_up(((m_cap + BM - 1) / BM + E) * n_tiles, kXcds);
-  if (blocks > 0x7FFFFFFF) return MX_EINVAL;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)blocks);
-  const bool direct = K % 128 == 0;
-  if (out_dtype == MX_OUT_F32) {
-    if (direct) launch_rows<true, true>(grid, st, a_q, a_s, b_q, b_s, offsets, E, m_cap, N, K, out);
-    else launch_rows<true, false>(grid, st, a_q, a_s, b_q, b_s, offsets, E, m_cap, N, K, out);
-  } else {
-    if (direct) launch_rows<false, true>(grid, st, a_q, a_s, b_q, b_s, offsets, E, m_cap, N, K, out);
-    else launch_rows<false, false>(grid, st, a_q, a_s, b_q, b_s, offsets, E, m_cap, N, K, out);
-  }
-  return launch_status();
+  if (((m_cap + BM - 1) / BM + E) * ((N + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  const RowsProblem p{a_q, a_s, b_q, b_s, m_cap, N, K, out, out_dtype == MX_OUT_F32};
+  return launch_any<false>(p, K % 128 == 0, offsets, E, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int mx_grouped_gemm_fwd(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
@@ -395,17 +569,8 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
   if (num_groups < 1 || m_cap < 0 || m_cap % 32 || n <= 0 || k <= 0 || n % 32 || k % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * m_cap >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile
-  const int64_t blocks = round_up((int64_t)num_groups * ((n + BM - 1) / BM) * ((k + BN - 1) / BN), kXcds);
-  if (blocks > 0x7FFFFFFF) return MX_EINVAL;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const dim3 grid((unsigned)blocks);
-  const bool direct = m_cap % 128 == 0;
-  if (out_dtype == MX_OUT_F32) {
-    if (direct) launch_wgrad<true, true>(grid, st, dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m_cap, n, k, dw);
-    else launch_wgrad<true, false>(grid, st, dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m_cap, n, k, dw);
-  } else {
-    if (direct) launch_wgrad<false, true>(grid, st, dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m_cap, n, k, dw);
-    else launch_wgrad<false, false>(grid, st, dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m_cap, n, k, dw);
-  }
-  return launch_status();
+  if (num_groups > kMaxGroups) return MX_EUNSUPPORTED;
+  if ((int64_t)num_groups * ((n + BM - 1) / BM) * ((k + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  const RowsProblem p{dyt_q, dyt_s, xt_q, xt_s, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
+  return launch_any<true>(p, m_cap % 128 == 0, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
 }

@@ -78,6 +78,14 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return v > o ? v : o;
 }
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (low half = a), round to nearest even
+// (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((v2f){a, b}, v2bf));
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite and infinite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);

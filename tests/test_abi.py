@@ -84,6 +84,7 @@ def test_gemm_validation(lib):
         assert fn(P, P, P, P, P, 2, 64, 64, 64, P, 7, None) == mxa.MX_EINVAL   # dtype
         assert fn(P, P, None, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL
         assert fn(P, P, P, P, P, 2, 0, 64, 64, P, 0, None) == mxa.MX_OK        # no rows: nothing to do
+        assert fn(P, P, P, P, P, 5000, 64, 64, 64, P, 0, None) == mxa.MX_EUNSUPPORTED  # too many groups
     w = lib.mx_grouped_gemm_wgrad
     assert w(P, P, P, P, P, 2, 48, 64, 64, P, 0, None) == mxa.MX_EINVAL        # m_cap % 32
     assert w(P, P, P, P, None, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL

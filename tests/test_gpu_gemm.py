@@ -154,3 +154,19 @@ def test_gemm_deterministic():
     r1 = run_rows("fwd", a_q, a_s, b_q, b_s, [0, 256], 256, 512, mxa.MX_OUT_F32)
     r2 = run_rows("fwd", a_q, a_s, b_q, b_s, [0, 256], 256, 512, mxa.MX_OUT_F32)
     assert np.array_equal(r1, r2)
+
+
+def test_bf16_epilogue_is_rne_of_fp32_accumulator():
+    """The bf16 output of a GEMM is the round-to-nearest-even of the fp32
+    output of the same call (same accumulation), element for element."""
+    g = np.random.default_rng(9)
+    sizes = [300, 0, 517, 64]
+    ids = workloads.ids_from_sizes(sizes)
+    counts, off, dst, src = routing.route(ids, 4)
+    a_q, a_s = routing.permute(*mx_rows(g, (sum(sizes), 640), 1.0, 0.01), src)
+    b_q, b_s = mx_rows(g, (4 * 384, 640), 0.02, 0.01)
+    b_q, b_s = b_q.reshape(4, 384, 640), b_s.reshape(4, 384, 20)
+    f32 = run_rows("fwd", a_q, a_s, b_q, b_s, off, 384, 640, mxa.MX_OUT_F32)
+    b16 = run_rows("fwd", a_q, a_s, b_q, b_s, off, 384, 640, mxa.MX_OUT_BF16)
+    lo, hi = int(off[0]), int(off[-1])
+    assert np.array_equal(b16[lo:hi], mx.f64_to_bf16(f32[lo:hi]))
