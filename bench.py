@@ -21,6 +21,7 @@ sample (one expert's share of the step).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -33,6 +34,28 @@ sys.path.insert(0, ROOT)
 PEAK_MXFP8_TFLOPS = 5000.0   # MI355X dense FP8/MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
 METRIC = "MXFP8 grouped-GEMM TFLOP/s fwd+bwd and quantize GB/s, % of MI355X peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CALIB_BYTES = 1 << 30        # plain device copy used to scale the FETCH_SIZE / WRITE_SIZE counters
+
+
+def measured_traffic(stage):
+    """HBM bytes per launch of ``stage`` as recorded in profiles/hbm_traffic.txt
+    (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or
+    None when no record exists or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    for line in open(TRAFFIC_FILE):
+        if not line.startswith("stage="):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        if kv.get("stage") != stage:
+            continue
+        src = os.path.join(ROOT, kv["source"])
+        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+            return None
+        return {"fetch_bytes": float(kv["fetch_bytes"]), "write_bytes": float(kv["write_bytes"]),
+                "bytes": float(kv["fetch_bytes"]) + float(kv["write_bytes"])}
+    return None
 
 
 def ensure_built():
@@ -105,10 +128,13 @@ def gpu_expert_path(args, c):
     dom = max(work["gemm_flops"], key=lambda n: per[n])
     dom_tf = work["gemm_flops"][dom] / (per[dom] * 1e-3) / 1e12
     counts = np.bincount(c["expert_ids"].ravel(), minlength=E)
+    tr = measured_traffic(dom)
     result = {
         "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4),
+                     "traffic": None if tr is None else tr["bytes"],
+                     "traffic_detail": tr, "algorithmic_operand_bytes": work["gemm_operand_bytes"][dom],
                      "per_launch_flops": work["gemm_flops"][dom], "avg_launch_ms": round(per[dom], 4)},
         "config": {"workload": "large expert GEMM fwd+dgrad+wgrad: T=8192 tokens, top-2 of E=16 experts "
                                "(16384 routed rows, >=1 empty expert), hidden K=5120, ffn N=8192, "
@@ -157,6 +183,20 @@ def gpu_quantize_bandwidth(args):
     del x, q, s, qt, st, y, yt
     torch.cuda.empty_cache()
     return out
+
+
+def copy_calibration():
+    """A plain device-to-device copy of CALIB_BYTES, three launches: the
+    reference the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    import torch
+    a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(args, c):
@@ -210,6 +250,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant-bench", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the expert path has no multi-GPU leg in this build "
@@ -227,6 +269,8 @@ def main():
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)
+    if args.copy_calibration:
+        copy_calibration()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, c)
     print(json.dumps(line), flush=True)

@@ -95,10 +95,16 @@ def algorithmic_work(T, K, N, E, topk, m_real=None):
     M = T * topk if m_real is None else m_real
     cap = -(-(T * topk + 31 * E) // 32) * 32
     gemm = 2.0 * M * N * K
+    # operand and output bytes each GEMM must move at least once: A and B codes
+    # plus scales (1 + 1/32 B per element) and a bf16 output
+    fwd_b = (M * K + E * N * K) * (1 + 1 / 32) + M * N * 2
+    dgrad_b = (M * N + E * K * N) * (1 + 1 / 32) + M * K * 2
+    wgrad_b = (N * M + K * M) * (1 + 1 / 32) + E * N * K * 2
     row_b = lambda r, c: r * c * (2 + 1 + 1 / 32)              # noqa: E731  bf16 in, codes + scales out
     rowcol_b = lambda r, c: r * c * (2 + 2 * (1 + 1 / 32))     # noqa: E731
     return {
         "gemm_flops": {"gemm_fwd": gemm, "gemm_dgrad": gemm, "gemm_wgrad": gemm},
+        "gemm_operand_bytes": {"gemm_fwd": fwd_b, "gemm_dgrad": dgrad_b, "gemm_wgrad": wgrad_b},
         "bytes": {
             "quant_x": row_b(T, K),
             "permute": K * (1 + 1 / 32) * (T + cap) + 4 * (T * topk * 2 + cap),
