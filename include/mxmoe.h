@@ -17,10 +17,18 @@
  * floor(log2(amax)) - 8 clamped to [-127, 127] (all-zero block -> byte 0);
  * element code = round-to-nearest-even of x / 2^scale, saturating at 448.
  *
- * Layouts (all row-major, device memory, caller-owned):
- *   bf16 tensors      uint16 bit patterns
- *   rowwise MX of [R, C]      q uint8 [R, C],  s uint8 [R, C/32]
- *   columnwise MX of [R, C]   stored transposed: q uint8 [C, R], s uint8 [C, R/32]
+ * Layouts (device memory, caller-owned):
+ *   bf16 tensors      uint16 bit patterns, row-major
+ *   MX tensor viewed as a matrix of R rows (batch entries stacked) and C
+ *   columns, blocks of 32 along C:
+ *     codes   q uint8 [R, C] row-major
+ *     scales  s uint8 [P, R, 4], P = ceil(C / 128) panels of 128 columns:
+ *             byte of (row r, block b) at ((b / 4) * R + r) * 4 + b % 4, so
+ *             one GEMM k step reads consecutive rows' scales as consecutive
+ *             dwords; bytes past the last block (C % 128 != 0) are zero.
+ *             4-byte aligned.  Written "scales [R, C]" below.
+ *   rowwise MX of [R, C]      q [R, C],  scales [R, C]
+ *   columnwise MX of [R, C]   stored transposed: q [C, R], scales [C, R]
  *                             (blocks are 32 consecutive rows of one column)
  *   expert weights    W [E, N, K] (K contiguous); W^T colwise [E, K, N]
  *   grouped rows      rows of expert e are [off[e], off[e+1]) of an M_cap-row
@@ -72,10 +80,10 @@ const char* mx_status_string(int status);
  *            entries >= rows also give zero rows.  Without a gather, output
  *            row r is source row r for r < rows and zero after.
  *   rows_out rows of the quantized output (per batch item)
- *   row_q/row_s  rowwise result [batch, rows_out, cols] / [batch, rows_out, cols/32],
- *            or both NULL to skip it
- *   col_q/col_s  columnwise result stored transposed [batch, cols, rows_out] /
- *            [batch, cols, rows_out/32], or both NULL to skip it
+ *   row_q/row_s  rowwise result: codes [batch, rows_out, cols], scales
+ *            [batch * rows_out, cols]; or both NULL to skip it
+ *   col_q/col_s  columnwise result stored transposed: codes [batch, cols,
+ *            rows_out], scales [batch * cols, rows_out]; or both NULL
  * One kernel reads x once and writes every requested output.  Requires
  * cols % 32 == 0; rows_out % 32 == 0 when a columnwise output is asked for;
  * at least one output.  Expert groups laid out at multiples of 32 with zero
@@ -89,7 +97,7 @@ int mx_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, co
  * MXFP8 dequantize (PR #3203 stacked list: MXFP8 dequantization kernel and
  * the e8m0 -> fp32 scale decode).  y = RNE_bf16(decode(q) * 2^(s-127)),
  * bf16 subnormals kept, overflow to Inf, NaN codes or scale 255 -> NaN.
- *   q uint8 [rows, cols], s uint8 [rows, cols/32] (blocks along cols),
+ *   q uint8 [rows, cols], s scales [rows, cols] (blocks along cols),
  *   y bf16 [rows, cols].  A columnwise tensor is dequantized as the
  *   [cols, rows] matrix it is stored as.  Requires cols % 32 == 0.
  */
@@ -104,11 +112,11 @@ size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_exper
  * MXFP8; TransformerEngine issue #556, first maintainer reply: fp8 data
  * moves as bytes as long as its scales move with it).
  *
- *   q, s          rowwise MX tokens [tokens, cols] / [tokens, cols/32]
+ *   q, s          rowwise MX tokens: codes [tokens, cols], scales [tokens, cols]
  *                 (both NULL, with q_out/s_out NULL: metadata only)
  *   expert_ids    int32 [tokens, topk]; flat pair i = t*topk + j
  *   capacity_rows rows of the permuted buffers, >= tokens*topk + 31*num_experts
- *   q_out, s_out  [capacity_rows, cols] / [capacity_rows, cols/32]
+ *   q_out, s_out  codes [capacity_rows, cols], scales [capacity_rows, cols]
  *   group_offsets int32 [num_experts+1]: expert e owns rows [off[e], off[e+1]);
  *                 every group is padded to a multiple of 32 rows
  *   dst_row       int32 [tokens*topk]: permuted row of pair i (-1 if its id
@@ -132,6 +140,8 @@ int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols,
  * accumulation in fp32.  out_dtype is MX_OUT_BF16 (RNE) or MX_OUT_F32.
  * Sizes: n % 32 == 0, k % 32 == 0, m_cap >= 0, num_groups >= 1.
  *
+ * Scales are in the panel layout above, of the whole operand matrix
+ * (b_s of W [E, n, k] is scales [E * n, k]).
  * fwd:   a = X_perm rowwise [m_cap, k], b = W rowwise [E, n, k],
  *        out Y [m_cap, n].  Rows of group e multiply W_e; rows outside every
  *        group are not written.

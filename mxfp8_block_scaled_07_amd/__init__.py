@@ -107,6 +107,14 @@ def mx_grouped_gemm_wgrad(dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m
 
 
 # --- allocating helpers ----------------------------------------------------
+def scale_shape(rows, cols):
+    """Shape of the scale bytes of an MX tensor with ``rows`` rows (batch
+    entries stacked) and ``cols`` columns, in the kernels' panel layout:
+    (ceil(cols / 128), rows, 4) -- panel p, row r holds the scale bytes of
+    blocks 4p..4p+3 of that row; pad bytes past the last block are zero."""
+    return ((cols + 127) // 128, rows, 4)
+
+
 def quantize(x, rowwise=True, colwise=False, rows_out=None, gather=None, stream=None):
     """x: bf16 (or int16 bit) tensor [rows, cols] or [batch, rows, cols] on the GPU.
     Returns (row_q, row_s, col_q, col_s); unrequested outputs are None."""
@@ -119,18 +127,19 @@ def quantize(x, rowwise=True, colwise=False, rows_out=None, gather=None, stream=
     dev = x.device
     shp = (rows_out, cols) if x.dim() == 2 else (batch, rows_out, cols)
     row_q = torch.empty(shp, dtype=torch.uint8, device=dev) if rowwise else None
-    row_s = torch.empty(shp[:-1] + (cols // 32,), dtype=torch.uint8, device=dev) if rowwise else None
+    row_s = torch.empty(scale_shape(batch * rows_out, cols), dtype=torch.uint8, device=dev) if rowwise else None
     cshp = (cols, rows_out) if x.dim() == 2 else (batch, cols, rows_out)
     col_q = torch.empty(cshp, dtype=torch.uint8, device=dev) if colwise else None
-    col_s = torch.empty(cshp[:-1] + (rows_out // 32,), dtype=torch.uint8, device=dev) if colwise else None
+    col_s = torch.empty(scale_shape(batch * cols, rows_out), dtype=torch.uint8, device=dev) if colwise else None
     mx_quantize(x, batch, rows, cols, gather, rows_out, row_q, row_s, col_q, col_s, stream)
     return row_q, row_s, col_q, col_s
 
 
 def dequantize(q, s, stream=None):
+    """q: codes [..., cols] (leading dims stacked as rows), s: panel-layout scales."""
     import torch
     y = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
-    mx_dequantize(q, s, q.shape[-2] if q.dim() > 1 else 1, q.shape[-1], y, stream)
+    mx_dequantize(q, s, q.numel() // q.shape[-1], q.shape[-1], y, stream)
     return y
 
 
@@ -143,7 +152,7 @@ def permute(q, s, expert_ids, num_experts, capacity_rows=None, stream=None):
     cap = -(-(tokens * topk + 31 * num_experts) // 32) * 32 if capacity_rows is None else capacity_rows
     cols = q.shape[1] if q is not None else 0
     q_out = torch.empty((cap, cols), dtype=torch.uint8, device=dev) if q is not None else None
-    s_out = torch.empty((cap, cols // 32), dtype=torch.uint8, device=dev) if q is not None else None
+    s_out = torch.empty(scale_shape(cap, cols), dtype=torch.uint8, device=dev) if q is not None else None
     off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
     dst = torch.empty(tokens * topk, dtype=torch.int32, device=dev)
     src = torch.empty(cap, dtype=torch.int32, device=dev)

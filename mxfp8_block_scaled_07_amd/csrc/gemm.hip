@@ -59,21 +59,27 @@ constexpr uint32_t kOob = 0x80000000u;                       // voffset that rea
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 // One operand tile: rows [0, rows) of a matrix starting at the tile's first
-// row, ld bytes per row, scales ld/32 bytes per row.
+// row, ld bytes per row.  Scales in the panel layout: the dword of (panel p,
+// tile row r) sits at p * pstride + 4 r from the tile's first scale dword.
 struct TileSrc {
   __amdgpu_buffer_rsrc_t q, s;
-  const uint8_t* sp;
   int64_t ld;
+  int32_t pstride;
   int rows;
 };
 
-__device__ __forceinline__ TileSrc make_src(const uint8_t* q, const uint8_t* s, int64_t ld, int64_t row0, int64_t rows) {
+// q, s: codes and scale dword of the matrix's row 0; pstride = 4 x the rows
+// of the whole scale panel (all groups / experts).
+__device__ __forceinline__ TileSrc make_src(const uint8_t* q, const uint8_t* s, int64_t ld, int64_t pstride,
+                                            int64_t row0, int64_t rows) {
   TileSrc t;
   const int64_t span = (int64_t)BM * ld;  // < 2^31 (checked on the host)
   t.q = __builtin_amdgcn_make_buffer_rsrc((void*)(q + row0 * ld), (short)0, (int)span, 0x00020000);
-  t.s = __builtin_amdgcn_make_buffer_rsrc((void*)(s + row0 * (ld >> 5)), (short)0, (int)(span >> 5), 0x00020000);
-  t.sp = s + row0 * (ld >> 5);
+  // every panel of the tile's rows: < 2^31 bytes (checked on the host)
+  const int64_t sspan = ((ld + 127) >> 7) * pstride;
+  t.s = __builtin_amdgcn_make_buffer_rsrc((void*)(s + row0 * 4), (short)0, (int)sspan, 0x00020000);
   t.ld = ld;
+  t.pstride = (int32_t)pstride;
   t.rows = rows < BM ? (int)rows : BM;
   return t;
 }
@@ -97,29 +103,14 @@ __device__ __forceinline__ void load_codes_blk(const TileSrc& t, uint8_t* lds_ti
   __builtin_amdgcn_raw_ptr_buffer_load_lds(t.q, (lds_void*)(lds_tile + blk * 1024), 16, voff, 0, 0, 0);
 }
 
-// The 4 scale bytes of the k step for each of the tile's 256 rows -> one
-// dword per row.  Direct path: ld is a multiple of 128 so the dword is aligned.
-__device__ __forceinline__ void load_scales_direct(const TileSrc& t, uint8_t* lds_sc, int64_t k0) {
+// The scale dword of the k step (panel k0 / 128) for each of the tile's 256
+// rows: the rows' dwords are contiguous in the panel layout.
+__device__ __forceinline__ void load_scales(const TileSrc& t, uint8_t* lds_sc, int64_t k0) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = 64 * w + lane;
-  const uint32_t voff = row < t.rows ? (uint32_t)row * (uint32_t)(t.ld >> 5) + (uint32_t)(k0 >> 5) : kOob;
+  const uint32_t voff = row < t.rows ? (uint32_t)(k0 >> 7) * (uint32_t)t.pstride + 4u * (uint32_t)row : kOob;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(t.s, (lds_void*)(lds_sc + w * 256), 4, voff, 0, 0, 0);
-}
-
-// Byte path (ld not a multiple of 128): gather the 4 bytes into a register
-// (branch free: a byte outside the row reads as zero).
-__device__ __forceinline__ uint32_t load_scales_bytes(const TileSrc& t, int64_t k0) {
-  const int row = threadIdx.x;
-  const int32_t nb = (int32_t)(t.ld >> 5);
-  uint32_t v = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int32_t b = (int32_t)(k0 >> 5) + j;
-    const uint32_t voff = ((row < t.rows) & (b < nb)) ? (uint32_t)row * (uint32_t)nb + (uint32_t)b : kOob;
-    v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(t.s, voff, 0, 0) << (8 * j);
-  }
-  return v;
 }
 
 __device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
@@ -246,8 +237,9 @@ __device__ __forceinline__ Tile rows_tile(const RowsProblem& p, const Sched& sc,
   const int64_t nt = rem / mt_e;
   const int64_t mt = rem - nt * mt_e;
   const int64_t row0 = lo + mt * BM;
-  t.A = make_src(p.a_q, p.a_s, p.K, row0, hi - row0);
-  t.B = make_src(p.b_q + (int64_t)e * p.N * p.K, p.b_s + (int64_t)e * p.N * (p.K >> 5), p.K, nt * BN, p.N - nt * BN);
+  t.A = make_src(p.a_q, p.a_s, p.K, 4 * p.m_cap, row0, hi - row0);
+  t.B = make_src(p.b_q + (int64_t)e * p.N * p.K, p.b_s + (int64_t)e * p.N * 4, p.K, 4 * (int64_t)E * p.N, nt * BN,
+                 p.N - nt * BN);
   t.k_begin = 0;
   t.k_lo = 0;
   t.k_hi = p.K;
@@ -277,8 +269,8 @@ __device__ __forceinline__ Tile wgrad_tile(const RowsProblem& p, const Sched& sc
   const int64_t nt = in_band / band_m;
   const int64_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);  // whole 32-blocks
   // here p.N is the dW row count and p.K its column count; the contraction runs over m_cap
-  t.A = make_src(p.a_q, p.a_s, p.m_cap, mt * BM, p.N - mt * BM);
-  t.B = make_src(p.b_q, p.b_s, p.m_cap, nt * BN, p.K - nt * BN);
+  t.A = make_src(p.a_q, p.a_s, p.m_cap, 4 * p.N, mt * BM, p.N - mt * BM);
+  t.B = make_src(p.b_q, p.b_s, p.m_cap, 4 * p.K, nt * BN, p.K - nt * BN);
   t.k_begin = lo & ~(int64_t)(BK - 1);
   t.k_lo = lo;
   t.k_hi = hi;
@@ -300,25 +292,18 @@ struct StageLoad {
   bool active;
 };
 
-template <bool kScaleDirect>
-__device__ __forceinline__ void issue_part(const StageLoad& sl, int i, uint32_t& sa_reg, uint32_t& sb_reg) {
+__device__ __forceinline__ void issue_part(const StageLoad& sl, int i) {
   load_codes_blk(sl.A, sl.dst, sl.k0, sl.k_lo, sl.k_hi, i);
   load_codes_blk(sl.B, sl.dst + kTileBytes, sl.k0, sl.k_lo, sl.k_hi, i);
   if (i == 0) {
-    if (kScaleDirect) {
-      load_scales_direct(sl.A, sl.dst + 2 * kTileBytes, sl.k0);
-      load_scales_direct(sl.B, sl.dst + 2 * kTileBytes + BM * 4, sl.k0);
-    } else {
-      sa_reg = load_scales_bytes(sl.A, sl.k0);
-      sb_reg = load_scales_bytes(sl.B, sl.k0);
-    }
+    load_scales(sl.A, sl.dst + 2 * kTileBytes, sl.k0);
+    load_scales(sl.B, sl.dst + 2 * kTileBytes + BM * 4, sl.k0);
   }
 }
 
-template <bool kScaleDirect>
-__device__ __forceinline__ void issue_stage(const StageLoad& sl, uint32_t& sa_reg, uint32_t& sb_reg) {
+__device__ __forceinline__ void issue_stage(const StageLoad& sl) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) issue_part<kScaleDirect>(sl, i, sa_reg, sb_reg);
+  for (int i = 0; i < 8; ++i) issue_part(sl, i);
 }
 
 // One k step of the wave's 128 x 128 sub-tile: 64 MFMAs, acc[i][j] covering
@@ -327,9 +312,7 @@ __device__ __forceinline__ void issue_stage(const StageLoad& sl, uint32_t& sa_re
 // The next stage's loads are issued two at a time between the MFMA rows:
 // issued back to back they stall the wave for thousands of cycles (memory
 // pipeline back-pressure) before the first MFMA.
-template <bool kScaleDirect>
-__device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], int wm, int wn, const StageLoad& sl,
-                                         uint32_t& sa_reg, uint32_t& sb_reg) {
+__device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], int wm, int wn, const StageLoad& sl) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int g = lane >> 4;
@@ -349,7 +332,7 @@ __device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], in
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    issue_part<kScaleDirect>(sl, i, sa_reg, sb_reg);
+    issue_part(sl, i);
     if (i < 7) {
       const int ra = wm * 128 + 16 * (i + 1) + r;
       af[(i + 1) & 1] = frag(At, ra, g);
@@ -369,7 +352,7 @@ __device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], in
   __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   /* DS read */       \
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     /* MFMA */
   __builtin_amdgcn_sched_group_barrier(0x100, 27, 0);  // A0, its scale, 8 B fragments and their scales
-  MX_ROW(kScaleDirect ? 4 : 10, 3)
+  MX_ROW(4, 3)
   MX_ROW(2, 3)
   MX_ROW(2, 3)
   MX_ROW(2, 3)
@@ -387,15 +370,6 @@ __device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], in
   for (int i = 0; i < 8; ++i)
     asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
                  "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
-}
-
-template <bool kScaleDirect>
-__device__ __forceinline__ void park_scales(uint8_t* st, uint32_t sa_reg, uint32_t sb_reg) {
-  if (!kScaleDirect) {
-    uint32_t* sc = reinterpret_cast<uint32_t*>(st + 2 * kTileBytes);
-    sc[threadIdx.x] = sa_reg;
-    sc[BM + threadIdx.x] = sb_reg;
-  }
 }
 
 __device__ __forceinline__ void zero_acc(v4f (&acc)[8][8]) {
@@ -423,13 +397,12 @@ struct TileGen {
 // statically, so the compiler sees that the reads of one never alias the
 // in-flight DMA writes of the other and does not wait for those loads
 // before reading.
-template <int CUR, bool kScaleDirect, typename Gen>
+template <int CUR, typename Gen>
 __device__ __forceinline__ void k_step(uint8_t* st0, uint8_t* st1, const Tile& cur, int s, bool has_next, int64_t Ln,
                                        const Gen& gen, bool& staged, v4f (&acc)[8][8], int wm, int wn) {
   uint8_t* comp = CUR ? st1 : st0;
   uint8_t* pre = CUR ? st0 : st1;
   __builtin_amdgcn_sched_barrier(0);  // keep each step's fragment reads inside the step
-  uint32_t sa_reg = 0, sb_reg = 0;
   StageLoad sl{cur.A, cur.B, pre, cur.k_begin + (int64_t)(s + 1) * BK, cur.k_lo, cur.k_hi, s + 1 < cur.steps};
   if (!sl.active && has_next) {
     const Tile nxt = gen(Ln);
@@ -442,8 +415,7 @@ __device__ __forceinline__ void k_step(uint8_t* st0, uint8_t* st1, const Tile& c
     sl.A.rows = sl.B.rows = 0;
     sl.k_hi = sl.k_lo;
   }
-  mma_step<kScaleDirect>(comp, acc, wm, wn, sl, sa_reg, sb_reg);
-  if (sl.active) park_scales<kScaleDirect>(pre, sa_reg, sb_reg);
+  mma_step(comp, acc, wm, wn, sl);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   __builtin_amdgcn_sched_barrier(0);
@@ -454,7 +426,7 @@ __device__ __forceinline__ void k_step(uint8_t* st0, uint8_t* st1, const Tile& c
 // XCD walk their range round robin.  The first k stage of the next tile is
 // loaded during the last k step of the current one, so tile changes cost no
 // exposed load latency and the epilogue stores overlap the next loads.
-template <bool kF32, bool kScaleDirect, bool kWgrad>
+template <bool kF32, bool kWgrad>
 __global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t* __restrict__ offsets, int32_t E) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
@@ -479,11 +451,9 @@ __global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t*
   bool staged = false;
   while (true) {
     if (cur.steps > 0 && !staged) {
-      uint32_t sa_reg = 0, sb_reg = 0;
       uint8_t* st = buf ? st1 : st0;
       const StageLoad sl{cur.A, cur.B, st, cur.k_begin, cur.k_lo, cur.k_hi, true};
-      issue_stage<kScaleDirect>(sl, sa_reg, sb_reg);
-      park_scales<kScaleDirect>(st, sa_reg, sb_reg);
+      issue_stage(sl);
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -491,13 +461,13 @@ __global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t*
     const bool has_next = Ln < L_end;
     staged = false;
     int s = 0;
-    if (buf && s < cur.steps) k_step<1, kScaleDirect>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
+    if (buf && s < cur.steps) k_step<1>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
     while (s + 1 < cur.steps) {
-      k_step<0, kScaleDirect>(st0, st1, cur, s, has_next, Ln, gen, staged, acc, wm, wn);
-      k_step<1, kScaleDirect>(st0, st1, cur, s + 1, has_next, Ln, gen, staged, acc, wm, wn);
+      k_step<0>(st0, st1, cur, s, has_next, Ln, gen, staged, acc, wm, wn);
+      k_step<1>(st0, st1, cur, s + 1, has_next, Ln, gen, staged, acc, wm, wn);
       s += 2;
     }
-    if (s < cur.steps) k_step<0, kScaleDirect>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
+    if (s < cur.steps) k_step<0>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
     buf = (buf + cur.steps) & 1;
     store_tile<kF32>(cur.out, cur.ldc, cur.m0, cur.A.rows, cur.n0, cur.n_end, acc, wm, wn);
     zero_acc(acc);
@@ -507,24 +477,19 @@ __global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t*
   }
 }
 
-template <bool kF32, bool kDirect, bool kWgrad>
+template <bool kF32, bool kWgrad>
 void launch(int ctas, hipStream_t st, const RowsProblem& p, const int32_t* off, int32_t E) {
-  hipLaunchKernelGGL((k_gemm<kF32, kDirect, kWgrad>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
+  hipLaunchKernelGGL((k_gemm<kF32, kWgrad>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
 }
 
 template <bool kWgrad>
-int launch_any(const RowsProblem& p, bool direct, const int32_t* off, int32_t E, hipStream_t st) {
+int launch_any(const RowsProblem& p, const int32_t* off, int32_t E, hipStream_t st) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MX_EHIP;
   const int ctas = (cus > 0 ? (cus + kXcds - 1) / kXcds : 1) * kXcds;
-  if (p.f32) {
-    if (direct) launch<true, true, kWgrad>(ctas, st, p, off, E);
-    else launch<true, false, kWgrad>(ctas, st, p, off, E);
-  } else {
-    if (direct) launch<false, true, kWgrad>(ctas, st, p, off, E);
-    else launch<false, false, kWgrad>(ctas, st, p, off, E);
-  }
+  if (p.f32) launch<true, kWgrad>(ctas, st, p, off, E);
+  else launch<false, kWgrad>(ctas, st, p, off, E);
   return launch_status();
 }
 
@@ -537,14 +502,17 @@ static int gemm_rows(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
                      const int32_t* offsets, int32_t E, int64_t m_cap, int64_t N, int64_t K, void* out,
                      int32_t out_dtype, mx_stream_t stream) {
   if (!a_q || !a_s || !b_q || !b_s || !offsets || !out) return MX_EINVAL;
+  if (((uintptr_t)a_s | (uintptr_t)b_s) & 3) return MX_EINVAL;  // scale dwords
   if (E < 1 || m_cap < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * K >= (1ll << 31) || m_cap >= (1ll << 31)) return MX_EINVAL;  // 32-bit tile spans and bounds
   if (E > kMaxGroups) return MX_EUNSUPPORTED;
   if (m_cap == 0) return MX_OK;
   if (((m_cap + BM - 1) / BM + E) * ((N + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  const int64_t panels = (K + 127) / 128;  // scale spans addressed with 32-bit offsets
+  if (panels * 4 * m_cap >= (1ll << 31) || panels * 4 * (int64_t)E * N >= (1ll << 31)) return MX_EINVAL;
   const RowsProblem p{a_q, a_s, b_q, b_s, m_cap, N, K, out, out_dtype == MX_OUT_F32};
-  return launch_any<false>(p, K % 128 == 0, offsets, E, reinterpret_cast<hipStream_t>(stream));
+  return launch_any<false>(p, offsets, E, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int mx_grouped_gemm_fwd(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
@@ -566,11 +534,14 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
                                      int64_t m_cap, int64_t n, int64_t k, void* dw, int32_t out_dtype,
                                      mx_stream_t stream) {
   if (!dyt_q || !dyt_s || !xt_q || !xt_s || !group_offsets || !dw) return MX_EINVAL;
+  if (((uintptr_t)dyt_s | (uintptr_t)xt_s) & 3) return MX_EINVAL;  // scale dwords
   if (num_groups < 1 || m_cap < 0 || m_cap % 32 || n <= 0 || k <= 0 || n % 32 || k % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * m_cap >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile
   if (num_groups > kMaxGroups) return MX_EUNSUPPORTED;
   if ((int64_t)num_groups * ((n + BM - 1) / BM) * ((k + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  const int64_t panels = (m_cap + 127) / 128;
+  if (panels * 4 * n >= (1ll << 31) || panels * 4 * k >= (1ll << 31)) return MX_EINVAL;
   const RowsProblem p{dyt_q, dyt_s, xt_q, xt_s, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
-  return launch_any<true>(p, m_cap % 128 == 0, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
+  return launch_any<true>(p, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
 }

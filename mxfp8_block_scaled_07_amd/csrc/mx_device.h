@@ -92,6 +92,24 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Scale layout of an MX tensor viewed as a matrix of R rows (batch entries
+// stacked) and C columns: 128-column panels, stored panel-major; inside
+// panel p, row r keeps the scale bytes of its blocks 4p..4p+3 in one dword.
+// A GEMM k step then reads the scales of consecutive rows as consecutive
+// dwords.  Byte of (row r, block b): ((b >> 2) * R + r) * 4 + (b & 3);
+// bytes of blocks past the last one (C % 128 != 0) are zero.
+__device__ __forceinline__ int64_t scale_index(int64_t R, int64_t r, int64_t b) {
+  return ((b >> 2) * R + r) * 4 + (b & 3);
+}
+
+// Store the scale byte of block b (of nb) of row r; the row's last block also
+// zeroes the pad bytes of its panel.
+__device__ __forceinline__ void put_scale(uint8_t* s, int64_t R, int64_t r, int64_t b, int64_t nb, uint32_t v) {
+  s[scale_index(R, r, b)] = (uint8_t)v;
+  if (b == nb - 1)
+    for (int64_t j = b + 1; j < ((nb + 3) & ~(int64_t)3); ++j) s[scale_index(R, r, j)] = 0;
+}
+
 inline int launch_status() { return hipGetLastError() == hipSuccess ? MX_OK : MX_EHIP; }
 
 }  // namespace mx

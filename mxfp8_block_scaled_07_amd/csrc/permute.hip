@@ -126,10 +126,12 @@ __global__ void __launch_bounds__(256) k_permute_rows(const uint8_t* __restrict_
   const uint4* qs = reinterpret_cast<const uint4*>(q + (ok ? src : 0) * cols);
   uint4* qd = reinterpret_cast<uint4*>(q_out + r * cols);
   for (int64_t i = lane; i < nq; i += 64) qd[i] = ok ? qs[i] : make_uint4(0, 0, 0, 0);
-  const int64_t ns = cols >> 5;  // scale bytes
-  const uint8_t* ss = s + (ok ? src : 0) * ns;
-  uint8_t* sd = s_out + r * ns;
-  for (int64_t i = lane; i < ns; i += 64) sd[i] = ok ? ss[i] : (uint8_t)0;
+  // scales: one dword per 128-column panel (panel-major layout, pad bytes
+  // travel with their row)
+  const int64_t np = (cols + 127) >> 7;
+  const uint32_t* ss = reinterpret_cast<const uint32_t*>(s);
+  uint32_t* sd = reinterpret_cast<uint32_t*>(s_out);
+  for (int64_t p = lane; p < np; p += 64) sd[p * capacity + r] = ok ? ss[p * tokens + src] : 0u;
 }
 
 }  // namespace
@@ -153,6 +155,7 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > 65536) return MX_EINVAL;
   if (!group_offsets || !src_row || (tokens > 0 && (!expert_ids || !dst_row))) return MX_EINVAL;
   if (copy && (!q || !s || !q_out || !s_out || cols <= 0 || cols % 32)) return MX_EINVAL;
+  if (copy && (((uintptr_t)s | (uintptr_t)s_out) & 3)) return MX_EINVAL;  // scale dwords
   const int64_t n = tokens * topk;
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
   if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;

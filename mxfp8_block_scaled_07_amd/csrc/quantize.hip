@@ -47,7 +47,7 @@ __global__ void __launch_bounds__(256) k_quant_rows(const uint16_t* __restrict__
   const float sc = e8m0_to_f32(sb);
   const uint2 out = make_uint2(cvt4_e4m3(v.x, v.y, sc), cvt4_e4m3(v.z, v.w, sc));
   *reinterpret_cast<uint2*>(q + row * cols + ch * 8) = out;
-  if ((ch & 3) == 0) s[row * (cols >> 5) + (ch >> 2)] = (uint8_t)sb;
+  if ((ch & 3) == 0) put_scale(s, total_rows, row, ch >> 2, cols >> 5, sb);
 }
 
 // ---------------------------------------------------------------------------
@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(256) k_quant_cols(const uint16_t* __restrict__
         const int64_t orow = b * rows_out + r;
         *reinterpret_cast<uint2*>(row_q + orow * cols + c0 + ch * 8) =
             make_uint2(cvt4_e4m3(v.x, v.y, sc), cvt4_e4m3(v.z, v.w, sc));
-        if ((ch & 3) == 0) row_s[orow * (cols >> 5) + ((c0 + ch * 8) >> 5)] = (uint8_t)sb;
+        if ((ch & 3) == 0) put_scale(row_s, (int64_t)gridDim.z * rows_out, orow, (c0 + ch * 8) >> 5, cols >> 5, sb);
       }
     }
     *reinterpret_cast<uint4*>(&tile[lr * kLdsStride + ch * 8]) = v;
@@ -135,7 +135,7 @@ __global__ void __launch_bounds__(256) k_quant_cols(const uint16_t* __restrict__
   uint8_t* dst = col_q + (b * cols + gc) * rows_out + gr;
   *reinterpret_cast<uint4*>(dst) = o0;
   *reinterpret_cast<uint4*>(dst + 16) = o1;
-  col_s[(b * cols + gc) * (rows_out >> 5) + (gr >> 5)] = (uint8_t)sb;
+  put_scale(col_s, (int64_t)gridDim.z * cols, b * cols + gc, gr >> 5, rows_out >> 5, sb);
 }
 
 // ---------------------------------------------------------------------------
@@ -148,7 +148,7 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ q, 
   const int64_t ch = (int64_t)blockIdx.y * 64 + (threadIdx.x & 63);
   if (row >= rows || ch >= (cols >> 4)) return;
   const uint4 c = *reinterpret_cast<const uint4*>(q + row * cols + ch * 16);
-  const uint32_t sb = s[row * (cols >> 5) + (ch >> 1)];
+  const uint32_t sb = s[scale_index(rows, row, ch >> 1)];
   uint4 o0, o1;
   if (sb == 255u) {  // E8M0 NaN scale: the whole block is NaN
     o0 = o1 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);

@@ -22,7 +22,7 @@ combine backward writes); ``zero_pad_rows`` prepares such a tensor.
 import torch
 
 from . import (MX_OUT_BF16, MX_OUT_F32, mx_grouped_gemm_dgrad, mx_grouped_gemm_fwd, mx_grouped_gemm_wgrad,
-               mx_permute, mx_permute_workspace_size, mx_quantize)
+               mx_permute, mx_permute_workspace_size, mx_quantize, scale_shape)
 
 STAGES = ("quant_x", "permute", "quant_w", "gemm_fwd", "quant_dy", "gemm_dgrad", "quant_xt", "gemm_wgrad")
 
@@ -38,16 +38,17 @@ class ExpertBuffers:
         od = torch.bfloat16 if out_dtype == MX_OUT_BF16 else torch.float32
         cap = self.cap
         e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=device)  # noqa: E731
-        self.xq, self.xs = e(T, K), e(T, K // 32)
-        self.xpq, self.xps = e(cap, K), e(cap, K // 32)
+        sc = lambda r, c: e(*scale_shape(r, c))  # noqa: E731  panel-layout scales
+        self.xq, self.xs = e(T, K), sc(T, K)
+        self.xpq, self.xps = e(cap, K), sc(cap, K)
         self.off, self.dst, self.src = e(E + 1, dt=i32), e(T * topk, dt=i32), e(cap, dt=i32)
         self.wsb = mx_permute_workspace_size(T, topk, E)
         self.ws = e(max(self.wsb, 4))
-        self.wq, self.wsc = e(E, N, K), e(E, N, K // 32)
-        self.wtq, self.wtsc = e(E, K, N), e(E, K, N // 32)
-        self.dyq, self.dys = e(cap, N), e(cap, N // 32)
-        self.dytq, self.dyts = e(N, cap), e(N, cap // 32)
-        self.xtq, self.xts = e(K, cap), e(K, cap // 32)
+        self.wq, self.wsc = e(E, N, K), sc(E * N, K)
+        self.wtq, self.wtsc = e(E, K, N), sc(E * K, N)
+        self.dyq, self.dys = e(cap, N), sc(cap, N)
+        self.dytq, self.dyts = e(N, cap), sc(N, cap)
+        self.xtq, self.xts = e(K, cap), sc(K, cap)
         self.y = e(cap, N, dt=od)
         self.dx = e(cap, K, dt=od)
         self.dw = e(E, N, K, dt=od)

@@ -58,3 +58,26 @@ def wgrad_h_fn(a_q, a_s, b_q, b_s, offsets, N, K):
                 out[sel] = tolerance.hardware_term(EA[n[sel], lo:hi], EB[k[sel], lo:hi])
         return out
     return fn
+
+
+def srows(sp, cols):
+    """Scale tensor in the kernels' panel layout ([ceil(cols/128), R, 4]
+    bytes: panel p, row r holds blocks 4p..4p+3) -> [R, cols/32] row-major,
+    the oracle's layout.  Also checks that the pad bytes are zero."""
+    a = host(sp) if isinstance(sp, torch.Tensor) else np.asarray(sp)
+    P, R, four = a.shape
+    assert four == 4 and P == -(-cols // 128), (a.shape, cols)
+    full = a.transpose(1, 0, 2).reshape(R, 4 * P)
+    nb = cols // 32
+    assert not full[:, nb:].any(), "pad bytes of the last scale panel must be zero"
+    return np.ascontiguousarray(full[:, :nb])
+
+
+def spanels(s):
+    """[R, nb] row-major scale bytes -> the kernels' panel layout [ceil(nb/4), R, 4]."""
+    s = np.asarray(s, np.uint8)
+    R, nb = s.shape
+    P = -(-nb // 4)
+    full = np.zeros((R, 4 * P), np.uint8)
+    full[:, :nb] = s
+    return np.ascontiguousarray(full.reshape(R, P, 4).transpose(1, 0, 2))

@@ -13,7 +13,7 @@ from oracle import gemm as og
 from oracle import mxfp8 as mx
 from oracle import routing, tolerance
 
-from gpu_util import dev, host, rows_h_fn, wgrad_h_fn
+from gpu_util import dev, host, rows_h_fn, spanels, wgrad_h_fn
 
 pytestmark = pytest.mark.gpu
 
@@ -24,7 +24,8 @@ def run_rows(kind, a_q, a_s, b_q, b_s, off, N, K, out_dtype, sentinel=True):
     dt = torch.float32 if out_dtype == mxa.MX_OUT_F32 else torch.bfloat16
     out = torch.full((M, N), 7.0 if sentinel else 0.0, dtype=dt, device="cuda:0")
     fn = mxa.mx_grouped_gemm_fwd if kind == "fwd" else mxa.mx_grouped_gemm_dgrad
-    fn(dev(a_q), dev(a_s), dev(b_q), dev(b_s), dev(np.asarray(off, np.int32)), E, M, N, K, out, out_dtype)
+    fn(dev(a_q), dev(spanels(a_s)), dev(b_q), dev(spanels(b_s.reshape(-1, b_s.shape[-1]))),
+       dev(np.asarray(off, np.int32)), E, M, N, K, out, out_dtype)
     torch.cuda.synchronize()
     return host(out) if out_dtype == mxa.MX_OUT_BF16 else host(out).astype(np.float64)
 
@@ -90,7 +91,8 @@ def check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, out_dtype):
     E = len(off) - 1
     dt = torch.float32 if out_dtype == mxa.MX_OUT_F32 else torch.bfloat16
     dw = torch.full((E, N, K), 7.0, dtype=dt, device="cuda:0")
-    mxa.mx_grouped_gemm_wgrad(dev(dyt_q), dev(dyt_s), dev(xt_q), dev(xt_s), dev(np.asarray(off, np.int32)), E, cap,
+    mxa.mx_grouped_gemm_wgrad(dev(dyt_q), dev(spanels(dyt_s)), dev(xt_q), dev(spanels(xt_s)),
+                              dev(np.asarray(off, np.int32)), E, cap,
                               N, K, dw, out_dtype)
     torch.cuda.synchronize()
     got = host(dw) if out_dtype == mxa.MX_OUT_BF16 else host(dw).astype(np.float64)

@@ -14,7 +14,7 @@ import workloads
 from oracle import mxfp8 as mx
 from oracle import routing
 
-from gpu_util import dev, host
+from gpu_util import dev, host, spanels, srows
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -29,7 +29,7 @@ def check_permute(ids, E, K=64, seed=0, copy=True, cap=None):
     q, s = mx.quantize_rowwise(xb)
     counts, off, dst, src = routing.route(ids, E, cap)
     qd = dev(q) if copy else None
-    sd = dev(s) if copy else None
+    sd = dev(spanels(s)) if copy else None
     q_out, s_out, goff, gdst, gsrc = mxa.permute(qd, sd, dev(ids), E, cap)
     torch.cuda.synchronize()
     assert np.array_equal(host(goff), off)
@@ -37,7 +37,7 @@ def check_permute(ids, E, K=64, seed=0, copy=True, cap=None):
     assert np.array_equal(host(gsrc), src)
     if copy:
         oq, os_ = routing.permute(q, s, src)
-        assert np.array_equal(host(q_out), oq) and np.array_equal(host(s_out), os_)
+        assert np.array_equal(host(q_out), oq) and np.array_equal(srows(s_out, K), os_)
     return host(gsrc)
 
 

@@ -14,7 +14,7 @@ from mxfp8_block_scaled_07_amd import MX_OUT_BF16, MX_OUT_F32, moe
 from oracle import mxfp8 as mx
 from oracle import routing, tolerance
 
-from gpu_util import dev, host
+from gpu_util import dev, host, srows
 
 pytestmark = pytest.mark.gpu
 
@@ -53,34 +53,36 @@ def test_expert_step_full_size(case, out_dtype):
     # X rowwise and its permuted copy (sampled rows)
     rows = np.sort(g.choice(T, 64, replace=False))
     oq, os_ = mx.quantize_rowwise(c["x"][rows])
-    assert np.array_equal(host(b.xq)[rows], oq) and np.array_equal(host(b.xs)[rows], os_)
+    assert np.array_equal(host(b.xq)[rows], oq) and np.array_equal(srows(b.xs, K)[rows], os_)
     prow = np.sort(g.choice(cap, 128, replace=False))
     pq, ps = routing.permute(*mx.quantize_rowwise(c["x"][np.maximum(src[prow], 0)]), np.where(src[prow] >= 0, np.arange(prow.size), -1))
     assert np.array_equal(host(b.xpq[torch.from_numpy(prow).cuda()]), pq)
-    assert np.array_equal(host(b.xps[torch.from_numpy(prow).cuda()]), ps)
+    assert np.array_equal(srows(b.xps, K)[prow], ps)
 
     # W rowwise and columnwise (two experts, sampled rows / columns)
     for e in [empty[0], int(g.integers(0, E))]:
         wr = np.sort(g.choice(N, 16, replace=False))
         oq, os_ = mx.quantize_rowwise(c["w"][e][wr])
-        assert np.array_equal(host(b.wq[e])[wr], oq) and np.array_equal(host(b.wsc[e])[wr], os_)
+        assert np.array_equal(host(b.wq[e])[wr], oq)
+        assert np.array_equal(srows(b.wsc, K)[e * N + wr], os_)
         wc = np.sort(g.choice(K, 16, replace=False))
         cq, cs = mx.quantize_rowwise(np.ascontiguousarray(c["w"][e][:, wc].T))
-        assert np.array_equal(host(b.wtq[e])[wc], cq) and np.array_equal(host(b.wtsc[e])[wc], cs)
+        assert np.array_equal(host(b.wtq[e])[wc], cq)
+        assert np.array_equal(srows(b.wtsc, N)[e * K + wc], cs)
 
     # dY row/col and X columnwise in permuted order (sampled)
     dr = np.sort(g.choice(cap, 32, replace=False))
     oq, os_ = mx.quantize_rowwise(dy_np[dr])
-    assert np.array_equal(host(b.dyq)[dr], oq) and np.array_equal(host(b.dys)[dr], os_)
+    assert np.array_equal(host(b.dyq)[dr], oq) and np.array_equal(srows(b.dys, N)[dr], os_)
     dc = np.sort(g.choice(N, 8, replace=False))
     cq, cs = mx.quantize_rowwise(np.ascontiguousarray(dy_np[:, dc].T))
     assert np.array_equal(host(b.dytq[torch.from_numpy(dc).cuda()]), cq)
-    assert np.array_equal(host(b.dyts[torch.from_numpy(dc).cuda()]), cs)
+    assert np.array_equal(srows(b.dyts, cap)[dc], cs)
     xc = np.sort(g.choice(K, 8, replace=False))
     xg = mx.gather_rows(c["x"][:, xc], src, cap)
     cq, cs = mx.quantize_rowwise(np.ascontiguousarray(xg.T))
     assert np.array_equal(host(b.xtq[torch.from_numpy(xc).cuda()]), cq)
-    assert np.array_equal(host(b.xts[torch.from_numpy(xc).cuda()]), cs)
+    assert np.array_equal(srows(b.xts, cap)[xc], cs)
 
     is_bf16 = out_dtype == MX_OUT_BF16
     nsamp = 384

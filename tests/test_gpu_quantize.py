@@ -14,7 +14,7 @@ import mxfp8_block_scaled_07_amd as mxa
 import workloads
 from oracle import mxfp8 as mx
 
-from gpu_util import dev, host
+from gpu_util import dev, host, spanels, srows
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -25,9 +25,20 @@ def gpu_quant(xb, rowwise=True, colwise=False, rows_out=None, gather=None, batch
     if batch is not None:
         x = x.view(batch, -1, xb.shape[-1])
     g = dev(np.asarray(gather, np.int32)) if gather is not None else None
-    out = mxa.quantize(x, rowwise=rowwise, colwise=colwise, rows_out=rows_out, gather=g)
+    q, s, qt, st = mxa.quantize(x, rowwise=rowwise, colwise=colwise, rows_out=rows_out, gather=g)
     torch.cuda.synchronize()
-    return [None if o is None else host(o) for o in out]
+    nb = 1 if batch is None else batch
+    cols = xb.shape[-1]
+    ro = x.shape[-2] if rows_out is None else rows_out
+    out = [None] * 4
+    if q is not None:   # scales back to [.., rows, cols/32] (pad bytes checked zero)
+        out[0] = host(q)
+        out[1] = srows(s, cols).reshape(q.shape[:-1] + (cols // 32,))
+    if qt is not None:
+        out[2] = host(qt)
+        out[3] = srows(st, ro).reshape(qt.shape[:-1] + (ro // 32,))
+        assert st.shape[1] == nb * cols
+    return out
 
 
 def test_golden_blocks():
@@ -90,9 +101,9 @@ def test_fused_rowcol_workload4_slice():
     cq, cs = mx.quantize_colwise(xb)
     assert np.array_equal(st, cs) and np.array_equal(qt, cq)
     # dequantize both orientations back to bf16
-    y = host(mxa.dequantize(dev(q), dev(s)))
+    y = host(mxa.dequantize(dev(q), dev(spanels(s))))
     assert np.array_equal(y, mx.dequantize(oq, os_))
-    yt = host(mxa.dequantize(dev(qt), dev(st)))
+    yt = host(mxa.dequantize(dev(qt), dev(spanels(st))))
     assert np.array_equal(yt, mx.dequantize(cq, cs))
 
 
@@ -112,10 +123,10 @@ def test_workload4_full_size_sampled():
     ridx = torch.from_numpy(rows).to(x.device)
     cidx = torch.from_numpy(cols).to(x.device)
     oq, os_ = mx.quantize_rowwise(xb[rows])
-    assert np.array_equal(host(q[ridx]), oq) and np.array_equal(host(s[ridx]), os_)
+    assert np.array_equal(host(q[ridx]), oq) and np.array_equal(srows(s[:, ridx], 5120), os_)
     assert np.array_equal(host(y[ridx]), mx.dequantize(oq, os_))
     cq, cs = mx.quantize_rowwise(np.ascontiguousarray(xb[:, cols].T))
-    assert np.array_equal(host(qt[cidx]), cq) and np.array_equal(host(st[cidx]), cs)
+    assert np.array_equal(host(qt[cidx]), cq) and np.array_equal(srows(st[:, cidx], 131072), cs)
     assert np.array_equal(host(yt[cidx]), mx.dequantize(cq, cs))
 
 
@@ -157,7 +168,7 @@ def test_dequantize_exhaustive_codes_and_scales():
     c, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
     q = np.repeat(c.reshape(-1, 1).astype(np.uint8), 32, axis=1)
     s = b.reshape(-1, 1).astype(np.uint8)
-    y = host(mxa.dequantize(dev(q), dev(s)))
+    y = host(mxa.dequantize(dev(q), dev(spanels(s))))
     ref = mx.dequantize(q, s)
     nan = np.isnan(mx.bf16_to_f64(ref))
     assert np.array_equal(np.isnan(mx.bf16_to_f64(y)), nan)
