@@ -3,159 +3,77 @@
 // digest "Key Questions Answered": the block-scaled matrix multiply applies the
 // per-block scales inside the matrix instruction (the Blackwell design
 // dequantizes through tensor memory; on CDNA4 the scales go straight into
-// V_MFMA_SCALE_F32_16X16X128_F8F6F4, so there is no dequantize step at all).
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4, so there is no dequantize step at all).
 // pytorch/ao PR #3203, "Next steps": the grouped GEMM takes pre-quantized
 // MXFP8 tensors (codes + scales).
 //
 // Every product is "NT": C[m, n] = sum_k A[m, k] B[n, k], both operands
-// contiguous along k, E8M0 scales [rows, k/32].  One kernel body serves
+// contiguous along k, scales in the panel layout of mx_device.h.  One kernel
+// body serves
 //   fwd / dgrad : rows of A grouped by expert (group e multiplies B_e)
 //   wgrad       : the contraction axis grouped by expert (dW_e = A_e . B_e^T)
 //
-// Scaled MFMA operand layout (16x16x128, E4M3 x E4M3, measured on gfx950):
-//   operand rows: lane l holds row (l & 15); with g = l >> 4 its bytes 0..15
-//      are k = 16g .. 16g+15 and bytes 16..31 are k = 64+16g .. 64+16g+15.
-//   scale: lane l supplies the E8M0 byte of (its row, 32-block g) of the
-//      128-wide k step (op_sel 0 reads bits 7:0 of the scale operand).
+// Scaled MFMA operand layout (32x32x64, E4M3 x E4M3, measured on gfx950):
+//   operand rows: lane l holds row (l & 31); with h = l >> 5 its bytes 0..15
+//      are k = 16h .. 16h+15 and bytes 16..31 are k = 32+16h .. 32+16h+15.
+//   scale: lane l supplies the E8M0 byte of (its row, 32-block h) of the
+//      64-wide k step (op_sel 0 reads bits 7:0 of the scale operand).
 //   D[i][j] = sum_k first[i][k] second[j][k]: lane l, register r holds
-//      D[4*(l >> 4) + r][l & 15].
-// The kernel passes the B tile as the first operand, so each lane ends up
-// holding 4 consecutive output columns of one output row.
+//      D[8 (r >> 2) + 4 h + (r & 3)][l & 31].
+// The kernel passes the B tile as the first operand, so each lane holds runs
+// of 4 consecutive output columns of one output row.
 //
 // Tiling: 256 x 256 output tile per 256-thread workgroup (one per CU), 2 x 2
-// waves of 128 x 128 (8 x 8 MFMA tiles each), k steps of 128.  Tiles are
-// staged in LDS by buffer loads that write LDS directly (no register round
-// trip); a load past a row or contraction bound returns zeros, which pads
-// ragged tiles for free.  Two LDS stages (2 x 66 KB): the loads of step s+1
-// fly while step s computes.  LDS rows are 128 B with the 16-byte chunks
-// XOR-swizzled by row so fragment reads are free of bank conflicts.
-// Workgroups are persistent (one per CU) and walk the output tiles of their
-// XCD's share in an order where concurrently running tiles share operand rows
-// in that XCD's L2.
+// waves of 128 x 128 (4 x 4 MFMA tiles of 32 x 32 each), k steps of 64.
+// Operand tiles reach LDS through buffer loads that write LDS directly; a
+// load past a row or contraction bound returns zeros, which pads ragged
+// tiles for free.  A ring of 4 LDS stages keeps three k steps in flight: the
+// loads of step s+3 are issued during step s, so L2-miss latency has more
+// than two steps to hide.  Each step runs its first 8 MFMAs, waits for stage
+// s+1 (one barrier per step), and reads the fragments of step s+1 from LDS
+// during its last 8 MFMAs, so a step never starts on an LDS read.
+// LDS rows are 64 B with the 16-byte chunks XOR-swizzled by row (conflict
+// free for the fragment reads).  Workgroups are persistent (one per CU) and
+// walk the output tiles of their XCD's share in an order where concurrently
+// running tiles share operand rows in that XCD's L2; the loads run ahead
+// across tile boundaries.
 
 #include "mx_device.h"
+
+// The LDS-direct loads below set M0 in inline asm (see dma16).
+#pragma clang diagnostic ignored "-Winline-asm"
 
 namespace mx {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kTileBytes = BM * BK;                          // one operand, one stage
-constexpr int kStageBytes = 2 * kTileBytes + 2 * BM * 4;     // A, B, A scales, B scales
+constexpr int kCodeBytes = BM * BK;                     // one operand, one stage (16 KB)
+constexpr int kScaleOff = 2 * kCodeBytes;               // A scale dwords, then B scale dwords
+constexpr int kStageBytes = 2 * kCodeBytes + 2 * BM * 4;
 constexpr int kXcds = 8;
-constexpr int kMaxGroups = 2048;                            // experts per grouped GEMM call
-constexpr uint32_t kOob = 0x80000000u;                       // voffset that reads as zero
+constexpr int kMaxGroups = 2048;                        // experts per grouped GEMM call
+constexpr uint32_t kOob = 0x80000000u;                  // voffset that reads as zero
+// Vector-memory instructions per wave per stage: 4 + 4 code blocks of 1 KB
+// and one scale dword per lane for A and for B.  kVmemFirst of them are
+// issued before the mid-step wait, the rest after it.
+constexpr int kVmem = 10;
+constexpr int kVmemFirst = 5;
 
-// 16-byte chunk swizzle of LDS row r.  ds_read_b128 serves 8 lanes (128 B)
-// at a time; the 8 rows read by one such group must hit 8 distinct chunk
-// columns.  Measured on gfx950: this XOR keeps fragment reads at the full
-// LDS rate (~240 B/clk/CU), where (r + r/8) & 7 reaches only ~150.  It
-// depends on r mod 16 only, so all fragments a lane reads share one chunk
-// column and differ by a constant (immediate) offset.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
+// bits 15:14, expcnt in 6:4, lgkmcnt in 11:8).
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
-// One operand tile: rows [0, rows) of a matrix starting at the tile's first
-// row, ld bytes per row.  Scales in the panel layout: the dword of (panel p,
-// tile row r) sits at p * pstride + 4 r from the tile's first scale dword.
-struct TileSrc {
-  __amdgpu_buffer_rsrc_t q, s;
-  int64_t ld;
-  int32_t pstride;
-  int rows;
-};
-
-// q, s: codes and scale dword of the matrix's row 0; pstride = 4 x the rows
-// of the whole scale panel (all groups / experts).
-__device__ __forceinline__ TileSrc make_src(const uint8_t* q, const uint8_t* s, int64_t ld, int64_t pstride,
-                                            int64_t row0, int64_t rows) {
-  TileSrc t;
-  const int64_t span = (int64_t)BM * ld;  // < 2^31 (checked on the host)
-  t.q = __builtin_amdgcn_make_buffer_rsrc((void*)(q + row0 * ld), (short)0, (int)span, 0x00020000);
-  // every panel of the tile's rows: < 2^31 bytes (checked on the host)
-  const int64_t sspan = ((ld + 127) >> 7) * pstride;
-  t.s = __builtin_amdgcn_make_buffer_rsrc((void*)(s + row0 * 4), (short)0, (int)sspan, 0x00020000);
-  t.ld = ld;
-  t.pstride = (int32_t)pstride;
-  t.rows = rows < BM ? (int)rows : BM;
-  return t;
-}
-
-// Codes of one operand tile, k window [k0, k0+128) with valid k in [k_lo, k_hi):
-// block i (of 8) of wave w, i.e. LDS block 8w+i of 1 KB (8 rows); lane l
-// writes slot l.
-__device__ __forceinline__ void load_codes_blk(const TileSrc& t, uint8_t* lds_tile, int64_t k0, int64_t k_lo,
-                                               int64_t k_hi, int i) {
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int blk = 8 * w + i;
-  const int row = 8 * blk + (lane >> 3);
-  const int c = (lane & 7) ^ swz(row);
-  // branch-free, 32-bit (tile spans are below 2^31): a lane-dependent branch
-  // here would split the step into divergent blocks and stop the scheduler
-  // from interleaving the loads with the MFMAs
-  const int32_t k = (int32_t)k0 + 16 * c;
-  const bool ok = (row < t.rows) & (k >= (int32_t)k_lo) & (k < (int32_t)k_hi);
-  const uint32_t voff = ok ? (uint32_t)row * (uint32_t)t.ld + (uint32_t)k : kOob;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(t.q, (lds_void*)(lds_tile + blk * 1024), 16, voff, 0, 0, 0);
-}
-
-// The scale dword of the k step (panel k0 / 128) for each of the tile's 256
-// rows: the rows' dwords are contiguous in the panel layout.
-__device__ __forceinline__ void load_scales(const TileSrc& t, uint8_t* lds_sc, int64_t k0) {
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = 64 * w + lane;
-  const uint32_t voff = row < t.rows ? (uint32_t)(k0 >> 7) * (uint32_t)t.pstride + 4u * (uint32_t)row : kOob;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(t.s, (lds_void*)(lds_sc + w * 256), 4, voff, 0, 0, 0);
-}
-
-__device__ __forceinline__ v8i frag(const uint8_t* tile, int row, int g) {
-  const int c = g ^ swz(row);
-  const uint4 lo = *reinterpret_cast<const uint4*>(tile + row * BK + 16 * c);
-  const uint4 hi = *reinterpret_cast<const uint4*>(tile + row * BK + 16 * (c ^ 4));
-  v8i v;
-  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-  return v;
-}
-
-// Rows [m0, m0 + rows) x cols [n0, n_end) of an output with ldc elements per row.
-template <bool kF32>
-__device__ __forceinline__ void store_tile(void* out, int64_t ldc, int64_t m0, int rows, int64_t n0, int64_t n_end,
-                                           const v4f (&acc)[8][8], int wm, int wn) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int ml = wm * 128 + 16 * i + (lane & 15);
-    if (ml >= rows) continue;
-    const int64_t m = m0 + ml;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t n = n0 + wn * 128 + 16 * j + 4 * (lane >> 4);
-      if (n >= n_end) continue;  // n_end % 32 == 0: the 4 columns are all in or all out
-      const v4f v = acc[i][j];
-      if (kF32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + m * ldc + n) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        const uint2 p = make_uint2(bf16x2_rne(v[0], v[1]), bf16x2_rne(v[2], v[3]));
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + m * ldc + n) = p;
-      }
-    }
-  }
-}
-
-// One output tile's work: operand sources, contraction window, destination.
-struct Tile {
-  TileSrc A, B;
-  int64_t k_begin, k_lo, k_hi;  // k steps start at k_begin; valid k in [k_lo, k_hi)
-  int steps;
-  void* out;
-  int64_t ldc, m0, n0, n_end;
-};
+// 16-byte chunk swizzle of LDS row r (rows are 64 B = 4 chunks).  The
+// fragment reads (ds_read_b128) of 8 or 16 consecutive lanes cover 8 or 16
+// consecutive rows at one chunk column; this XOR sends them to distinct bank
+// groups in both cases.  Depends on r mod 16 only.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 // Group schedule shared by the workgroup: clamped, monotone group bounds and
 // (row-grouped problems) the running count of tiles before each group.
@@ -221,269 +139,645 @@ __device__ __forceinline__ int find_group(const Sched& sc, int E, int64_t L) {
   return lo;
 }
 
-struct RowsProblem {
+struct Problem {
   const uint8_t *a_q, *a_s, *b_q, *b_s;
   int64_t m_cap, N, K;
   void* out;
   bool f32;
 };
 
-__device__ __forceinline__ Tile rows_tile(const RowsProblem& p, const Sched& sc, int E, int64_t n_tiles, int64_t L) {
-  Tile t;
-  const int e = find_group(sc, E, L);
-  const int64_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);
-  const int64_t mt_e = (hi - lo + BM - 1) / BM;
-  const int64_t rem = L - uni(sc.tiles_before[e]);
-  const int64_t nt = rem / mt_e;
-  const int64_t mt = rem - nt * mt_e;
-  const int64_t row0 = lo + mt * BM;
-  t.A = make_src(p.a_q, p.a_s, p.K, 4 * p.m_cap, row0, hi - row0);
-  t.B = make_src(p.b_q + (int64_t)e * p.N * p.K, p.b_s + (int64_t)e * p.N * 4, p.K, 4 * (int64_t)E * p.N, nt * BN,
-                 p.N - nt * BN);
-  t.k_begin = 0;
-  t.k_lo = 0;
-  t.k_hi = p.K;
-  t.steps = (int)((p.K + BK - 1) / BK);
-  t.out = p.out;
-  t.ldc = p.N;
-  t.m0 = row0;
-  t.n0 = nt * BN;
-  t.n_end = p.N;
-  return t;
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (the four dwords of a V#): base, stride 0,
+// num_records bytes, the same flags as __builtin_amdgcn_make_buffer_rsrc uses.
+__device__ __forceinline__ v4u rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return v4u{(uint32_t)a, (uint32_t)(a >> 32) & 0xFFFFu, (uint32_t)bytes, 0x00020000u};
 }
 
-// wgrad: tiles of an expert walked in bands of 4 m tiles, n-tile major inside
-// a band, so concurrently running tiles share A and B rows.
-__device__ __forceinline__ Tile wgrad_tile(const RowsProblem& p, const Sched& sc, int64_t m_tiles, int64_t n_tiles,
-                                           int64_t L) {
-  Tile t;
-  const int64_t per = m_tiles * n_tiles;
-  const int64_t e = L / per;
-  const int64_t rem = L - e * per;
-  constexpr int64_t kBand = 4;
-  const int64_t band = rem / (kBand * n_tiles);
-  const int64_t first_m = band * kBand;
-  const int64_t band_m = (m_tiles - first_m) < kBand ? (m_tiles - first_m) : kBand;
-  const int64_t in_band = rem - band * kBand * n_tiles;
-  const int64_t mt = first_m + in_band % band_m;
-  const int64_t nt = in_band / band_m;
-  const int64_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);  // whole 32-blocks
-  // here p.N is the dW row count and p.K its column count; the contraction runs over m_cap
-  t.A = make_src(p.a_q, p.a_s, p.m_cap, 4 * p.N, mt * BM, p.N - mt * BM);
-  t.B = make_src(p.b_q, p.b_s, p.m_cap, 4 * p.K, nt * BN, p.K - nt * BN);
-  t.k_begin = lo & ~(int64_t)(BK - 1);
-  t.k_lo = lo;
-  t.k_hi = hi;
-  t.steps = hi > lo ? (int)((hi - t.k_begin + BK - 1) / BK) : 0;
-  t.out = p.f32 ? (void*)(static_cast<float*>(p.out) + e * p.N * p.K) : (void*)(static_cast<uint16_t*>(p.out) + e * p.N * p.K);
-  t.ldc = p.K;
-  t.m0 = mt * BM;
-  t.n0 = nt * BN;
-  t.n_end = p.K;
-  return t;
-}
-
-// The loads of one k stage (A and B codes plus scales) into LDS stage dst,
-// issued in 8 parts so they can be spread between MFMAs.
-struct StageLoad {
-  TileSrc A, B;
-  uint8_t* dst;
-  int64_t k0, k_lo, k_hi;
-  bool active;
+// Where a tile's operands come from (the loader's view).
+struct LoadTile {
+  v4u aq, as, bq, bs;                      // codes / scales from the tile's first A and B rows
+  int32_t rows_a, rows_b;                  // valid rows (<= 256) of the two operand tiles
+  int32_t k_begin, k_lo, k_hi;             // k steps start at k_begin (a multiple of 128); valid k in [k_lo, k_hi)
+  int32_t steps;
 };
 
-__device__ __forceinline__ void issue_part(const StageLoad& sl, int i) {
-  load_codes_blk(sl.A, sl.dst, sl.k0, sl.k_lo, sl.k_hi, i);
-  load_codes_blk(sl.B, sl.dst + kTileBytes, sl.k0, sl.k_lo, sl.k_hi, i);
-  if (i == 0) {
-    load_scales(sl.A, sl.dst + 2 * kTileBytes, sl.k0);
-    load_scales(sl.B, sl.dst + 2 * kTileBytes + BM * 4, sl.k0);
-  }
-}
+// Where a tile's result goes (the compute side's view).
+struct OutTile {
+  void* out;
+  int64_t ldc, m0, n0, n_end;
+  int32_t rows;   // valid output rows
+  int32_t steps;
+};
 
-__device__ __forceinline__ void issue_stage(const StageLoad& sl) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) issue_part(sl, i);
-}
+// Tile coordinates of logical tile L.
+struct Coord {
+  int64_t e, row_a, row_b;  // group, first A row, first B row (within B_e for row problems)
+  int32_t rows_a, rows_b, k_begin, k_lo, k_hi, steps;
+};
 
-// One k step of the wave's 128 x 128 sub-tile: 64 MFMAs, acc[i][j] covering
-// A rows 16i.. and B rows 16j...  All 8 B fragments stay in registers; the A
-// fragments are double buffered so row i+1 is read while row i multiplies.
-// The next stage's loads are issued two at a time between the MFMA rows:
-// issued back to back they stall the wave for thousands of cycles (memory
-// pipeline back-pressure) before the first MFMA.
-__device__ __forceinline__ void mma_step(const uint8_t* st, v4f (&acc)[8][8], int wm, int wn, const StageLoad& sl) {
-  const int lane = threadIdx.x & 63;
-  const int r = lane & 15;
-  const int g = lane >> 4;
-  const uint8_t* At = st;
-  const uint8_t* Bt = st + kTileBytes;
-  const uint32_t* Sa = reinterpret_cast<const uint32_t*>(st + 2 * kTileBytes);
-  const uint32_t* Sb = Sa + BM;
-  v8i bf[8], af[2];
-  int sb[8], sa[2];
-  af[0] = frag(At, wm * 128 + r, g);
-  sa[0] = (int)(Sa[wm * 128 + r] >> (8 * g));
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int rb = wn * 128 + 16 * j + r;
-    bf[j] = frag(Bt, rb, g);
-    sb[j] = (int)(Sb[rb] >> (8 * g));
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    issue_part(sl, i);
-    if (i < 7) {
-      const int ra = wm * 128 + 16 * (i + 1) + r;
-      af[(i + 1) & 1] = frag(At, ra, g);
-      sa[(i + 1) & 1] = (int)(Sa[ra] >> (8 * g));
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf[j], af[i & 1], acc[i][j], 0, 0, 0, sb[j], 0,
-                                                                   sa[i & 1]);
-  }
-  // Instruction order for the machine scheduler (the MFMA builtins are pure
-  // and would otherwise all sink below the loads): the fragment reads first,
-  // then per row: its share of the next stage's loads, the next A fragment,
-  // and the row's 8 MFMAs.
-#define MX_ROW(nvmem, nds)                                                   \
-  __builtin_amdgcn_sched_group_barrier(0x020, nvmem, 0); /* VMEM read */     \
-  __builtin_amdgcn_sched_group_barrier(0x100, nds, 0);   /* DS read */       \
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     /* MFMA */
-  __builtin_amdgcn_sched_group_barrier(0x100, 27, 0);  // A0, its scale, 8 B fragments and their scales
-  MX_ROW(4, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 3)
-  MX_ROW(2, 0)
-#undef MX_ROW
-  __builtin_amdgcn_sched_barrier(0);
-  // The MFMA results are only consumed steps later, so the compiler would sink
-  // the whole step's MFMAs below the step's s_waitcnt / s_barrier and they
-  // would stop hiding the load latency.  An empty asm that claims to update
-  // the accumulators keeps them above it.
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
-                 "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
-}
-
-__device__ __forceinline__ void zero_acc(v4f (&acc)[8][8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-}
-
-// Tile source of the persistent loop (row-grouped or wgrad problems).
+// (32-bit tile arithmetic: tile counts are below 2^31, checked on the host;
+// 32-bit divisions are much shorter than 64-bit ones)
 template <bool kWgrad>
-struct TileGen {
-  const RowsProblem& p;
+__device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E, int64_t m_tiles, int64_t n_tiles,
+                                       int64_t L64) {
+  Coord c;
+  const uint32_t L = (uint32_t)L64;
+  if (!kWgrad) {
+    // rows of group e in tiles of 256; a group's tiles walked n-tile major
+    const int e = find_group(sc, E, L64);
+    const int32_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);
+    const uint32_t mt_e = (uint32_t)(hi - lo + BM - 1) / BM;
+    const uint32_t rem = L - (uint32_t)uni(sc.tiles_before[e]);
+    const uint32_t nt = rem / mt_e;
+    const uint32_t mt = rem - nt * mt_e;
+    c.e = e;
+    c.row_a = lo + (int64_t)mt * BM;
+    c.row_b = (int64_t)nt * BN;
+    c.rows_a = (int32_t)(hi - c.row_a < BM ? hi - c.row_a : BM);
+    c.rows_b = (int32_t)(p.N - c.row_b < BN ? p.N - c.row_b : BN);
+    c.k_begin = 0;
+    c.k_lo = 0;
+    c.k_hi = (int32_t)p.K;
+    c.steps = (int32_t)((p.K + BK - 1) / BK);
+  } else {
+    // dW_e tiles walked in bands of 4 m tiles, n-tile major inside a band, so
+    // concurrently running tiles share A and B rows
+    const uint32_t mtl = (uint32_t)m_tiles, ntl = (uint32_t)n_tiles;
+    const uint32_t per = mtl * ntl;
+    const uint32_t e = L / per;
+    const uint32_t rem = L - e * per;
+    constexpr uint32_t kBand = 4;
+    const uint32_t band = rem / (kBand * ntl);
+    const uint32_t first_m = band * kBand;
+    const uint32_t band_m = (mtl - first_m) < kBand ? (mtl - first_m) : kBand;
+    const uint32_t in_band = rem - band * kBand * ntl;
+    const uint32_t nt = in_band / band_m;
+    const uint32_t mt = first_m + (in_band - nt * band_m);
+    const int32_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);  // whole 32-blocks
+    // p.N is the dW row count, p.K its column count; the contraction runs over m_cap
+    c.e = e;
+    c.row_a = (int64_t)mt * BM;
+    c.row_b = (int64_t)nt * BN;
+    c.rows_a = (int32_t)(p.N - c.row_a < BM ? p.N - c.row_a : BM);
+    c.rows_b = (int32_t)(p.K - c.row_b < BN ? p.K - c.row_b : BN);
+    c.k_begin = lo & ~127;
+    c.k_lo = lo;
+    c.k_hi = hi;
+    c.steps = hi > lo ? (hi - c.k_begin + BK - 1) / BK : 0;
+  }
+  return c;
+}
+
+template <bool kWgrad>
+__device__ __forceinline__ LoadTile load_tile(const Problem& p, const Coord& c, int E) {
+  LoadTile t;
+  const int64_t ld = kWgrad ? p.m_cap : p.K;               // bytes per operand row
+  const int64_t pa = kWgrad ? 4 * p.N : 4 * p.m_cap;      // scale panel strides
+  const int64_t pb = kWgrad ? 4 * p.K : 4 * (int64_t)E * p.N;
+  const int64_t panels = (ld + 127) >> 7;
+  const uint8_t* bq = kWgrad ? p.b_q : p.b_q + c.e * p.N * p.K;
+  const uint8_t* bs = kWgrad ? p.b_s : p.b_s + c.e * p.N * 4;
+  // num_records: rows past the valid ones read as zero; every span is below
+  // 2^31 (checked on the host)
+  t.aq = rsrc(p.a_q + c.row_a * ld, c.rows_a * ld);
+  t.bq = rsrc(bq + c.row_b * ld, c.rows_b * ld);
+  t.as = rsrc(p.a_s + c.row_a * 4, panels * pa);
+  t.bs = rsrc(bs + c.row_b * 4, panels * pb);
+  t.rows_a = c.rows_a;
+  t.rows_b = c.rows_b;
+  t.k_begin = c.k_begin;
+  t.k_lo = c.k_lo;
+  t.k_hi = c.k_hi;
+  t.steps = c.steps;
+  return t;
+}
+
+template <bool kWgrad>
+__device__ __forceinline__ OutTile out_tile(const Problem& p, const Coord& c) {
+  OutTile o;
+  if (!kWgrad) {
+    o.out = p.out;
+    o.ldc = p.N;
+    o.n_end = p.N;
+  } else {
+    o.out = p.f32 ? (void*)(static_cast<float*>(p.out) + c.e * p.N * p.K)
+                  : (void*)(static_cast<uint16_t*>(p.out) + c.e * p.N * p.K);
+    o.ldc = p.K;
+    o.n_end = p.K;
+  }
+  o.m0 = c.row_a;
+  o.n0 = c.row_b;
+  o.rows = c.rows_a;
+  o.steps = c.steps;
+  return o;
+}
+
+// Everything needed to walk the workgroup's tiles.
+template <bool kWgrad>
+struct Walk {
+  const Problem& p;
   const Sched& sc;
   int E;
-  int64_t m_tiles, n_tiles;
-  __device__ __forceinline__ Tile operator()(int64_t l) const {
-    return kWgrad ? wgrad_tile(p, sc, m_tiles, n_tiles, l) : rows_tile(p, sc, E, n_tiles, l);
-  }
+  int64_t m_tiles, n_tiles, stride, L_end;
+  __device__ __forceinline__ Coord at(int64_t L) const { return coord<kWgrad>(p, sc, E, m_tiles, n_tiles, L); }
 };
 
-// One k step: MFMAs on LDS stage CUR while the next stage (the next k window
-// of this tile, or the first one of the next tile) streams into the other.
-// The two stages are distinct LDS objects and each step names them
-// statically, so the compiler sees that the reads of one never alias the
-// in-flight DMA writes of the other and does not wait for those loads
-// before reading.
-template <int CUR, typename Gen>
-__device__ __forceinline__ void k_step(uint8_t* st0, uint8_t* st1, const Tile& cur, int s, bool has_next, int64_t Ln,
-                                       const Gen& gen, bool& staged, v4f (&acc)[8][8], int wm, int wn) {
-  uint8_t* comp = CUR ? st1 : st0;
-  uint8_t* pre = CUR ? st0 : st1;
-  __builtin_amdgcn_sched_barrier(0);  // keep each step's fragment reads inside the step
-  StageLoad sl{cur.A, cur.B, pre, cur.k_begin + (int64_t)(s + 1) * BK, cur.k_lo, cur.k_hi, s + 1 < cur.steps};
-  if (!sl.active && has_next) {
-    const Tile nxt = gen(Ln);
-    if (nxt.steps > 0) {
-      sl = StageLoad{nxt.A, nxt.B, pre, nxt.k_begin, nxt.k_lo, nxt.k_hi, true};
-      staged = true;
+// Per-lane constants of the loads.  Code loads: lane l of wave w writes 16 B
+// of LDS block 4w + i (16 rows x 64 B): block row 16(4w + i) + l/4, LDS slot
+// l & 3, holding the global chunk (l & 3) ^ swz(row).  Scale loads: lane l
+// of wave w fetches the dword of tile row 64w + l.
+struct LaneLoads {
+  uint32_t voff[4];   // row * ld + 16 * chunk
+  int32_t kc[4];      // 16 * chunk
+  int32_t srow;       // 64 w + l
+};
+
+// k steps a tile occupies in the 4-stage ring: its own rounded up to a
+// multiple of 4, so every tile starts on stage 0 and the ring can be unrolled
+// with a single loop exit; the padding steps load zeros and add zeros.
+__device__ __forceinline__ int32_t ring_steps(int32_t steps) { return (steps + 3) & ~3; }
+
+// The loader walks the same tiles as the compute side, three k steps ahead,
+// skipping tiles without k steps.
+struct Loader {
+  LoadTile t;
+  int64_t L;
+  int32_t s;
+  bool valid;
+};
+
+template <bool kWgrad>
+__device__ __forceinline__ void loader_seek(Loader& ld, const Walk<kWgrad>& w) {
+  while (ld.valid && ld.s >= ring_steps(ld.t.steps)) {
+    ld.L += w.stride;
+    if (ld.L >= w.L_end) {
+      ld.valid = false;
+    } else {
+      ld.t = load_tile<kWgrad>(w.p, w.at(ld.L), w.E);
+      ld.s = 0;
     }
   }
-  if (!sl.active) {  // nothing to prefetch: every load of the stage becomes a zero read
-    sl.A.rows = sl.B.rows = 0;
-    sl.k_hi = sl.k_lo;
+}
+
+// One LDS-direct buffer load (16 B or 4 B per lane) into LDS at byte lds
+// (+ 16 or 4 x lane).  Written as inline asm so the compiler neither tracks
+// it nor adds waits for it: every wait on these loads is explicit (vmcnt in
+// stage_barrier), and the stage a load writes is never read before that
+// wait and a barrier.  M0 holds the LDS address; nothing else in these
+// kernels uses M0 (gfx9 LDS instructions do not read it).
+__device__ __forceinline__ void dma16(const v4u& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "m0");
+}
+
+__device__ __forceinline__ void dma4(const v4u& r, uint32_t lds, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+               : "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+
+// The loads of the loader's current k step into one LDS stage: 10
+// instructions per wave (A0 B0 A1 B1 A2 B2 A3 B3 sA sB), issued one by one
+// between the MFMAs.  A loader past its last tile issues the same
+// instructions with out-of-range offsets (they read zeros), so every step
+// issues exactly kVmem instructions per wave.
+struct LoadPlan {
+  v4u aq, bq, as, bs;
+  uint32_t v[4];       // code voffsets (out of range where the chunk is outside [k_lo, k_hi))
+  uint32_t soff;       // k0
+  uint32_t sa, sb;     // scale voffsets
+  uint32_t pa, pb;     // scale panel offsets
+  uint32_t dst;        // LDS address of the stage + this wave's first code block
+  uint32_t sdst;       // LDS address of the stage's scales + this wave's rows
+};
+
+__device__ __forceinline__ LoadPlan plan_loads(const Loader& ld, const LaneLoads& ll, const uint8_t* stage,
+                                               int64_t pstride_a, int64_t pstride_b) {
+  LoadPlan pl;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int32_t k0 = ld.t.k_begin + BK * ld.s;
+  // chunks outside [k_lo, k_hi) occur in a tile's first or last steps and in
+  // its padding steps (which read nothing but zeros)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t k = k0 + ll.kc[i];
+    const bool ok = ld.valid & (k >= ld.t.k_lo) & (k < ld.t.k_hi);
+    pl.v[i] = ok ? ll.voff[i] : kOob;
   }
-  mma_step(comp, acc, wm, wn, sl);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  pl.aq = ld.t.aq;
+  pl.bq = ld.t.bq;
+  pl.as = ld.t.as;
+  pl.bs = ld.t.bs;
+  pl.soff = ld.valid ? (uint32_t)k0 : 0u;
+  pl.sa = (ld.valid & (ll.srow < ld.t.rows_a)) ? 4u * (uint32_t)ll.srow : kOob;
+  pl.sb = (ld.valid & (ll.srow < ld.t.rows_b)) ? 4u * (uint32_t)ll.srow : kOob;
+  pl.pa = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_a : 0u;
+  pl.pb = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_b : 0u;
+  pl.dst = lds_addr(stage) + (uint32_t)(4 * w * 1024);
+  pl.sdst = lds_addr(stage) + (uint32_t)(kScaleOff + w * 256);
+  return pl;
+}
+
+// Load number n (0..9) of a plan.
+__device__ __forceinline__ void load_n(const LoadPlan& pl, int n) {
+  if (n < 8) {
+    const int i = n >> 1;
+    if (n & 1) dma16(pl.bq, pl.dst + kCodeBytes + i * 1024, pl.v[i], pl.soff);
+    else dma16(pl.aq, pl.dst + i * 1024, pl.v[i], pl.soff);
+  } else if (n == 8) {
+    dma4(pl.as, pl.sdst, pl.sa, pl.pa);
+  } else {
+    dma4(pl.bs, pl.sdst + BM * 4, pl.sb, pl.pb);
+  }
+}
+
+__device__ __forceinline__ void issue_all(const LoadPlan& pl) {
+#pragma unroll
+  for (int n = 0; n < kVmem; ++n) load_n(pl, n);
+}
+
+// The MFMA operands of one k step for one wave.  Scales hold the raw panel
+// dwords until shifted at the start of the step that uses them.
+struct Frags {
+  v8i a[4], b[4];
+  int sa[4], sb[4];
+};
+
+// Lane offsets of a fragment inside a 32-row block: row r = l & 31, chunks
+// h and h + 2 (h = l >> 5), swizzled.  swz depends on the row's bits 1..3
+// only, so rows 32 i + r of any block share these offsets and a fragment is
+// read at (block base) + offset with the block base an immediate.
+struct FragOff {
+  int lo, hi, sc;   // code chunk offsets, scale dword offset
+};
+
+__device__ __forceinline__ FragOff frag_off() {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 31, h = lane >> 5;
+  const int c = h ^ swz(r);
+  return FragOff{r * BK + 16 * c, r * BK + 16 * (c ^ 2), 4 * r};
+}
+
+__device__ __forceinline__ v8i frag(const uint8_t* blk, const FragOff& fo) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(blk + fo.lo);
+  const uint4 hi = *reinterpret_cast<const uint4*>(blk + fo.hi);
+  v8i v;
+  v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+  v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+  return v;
+}
+
+// Fragments of A blocks i0 .. i1-1 of a stage (with their scale dwords).
+__device__ __forceinline__ void read_a(const uint8_t* st, Frags& f, int wm, int i0, int i1, const FragOff& fo) {
+  const uint8_t* A = st + wm * 128 * BK;
+  const uint8_t* S = st + kScaleOff + wm * 128 * 4;
+#pragma unroll
+  for (int i = i0; i < i1; ++i) {
+    f.a[i] = frag(A + 32 * i * BK, fo);
+    f.sa[i] = *reinterpret_cast<const int*>(S + 32 * i * 4 + fo.sc);
+  }
+}
+
+// All 4 B fragments of a stage (with their scale dwords).
+__device__ __forceinline__ void read_b(const uint8_t* st, Frags& f, int wn, const FragOff& fo) {
+  const uint8_t* B = st + kCodeBytes + wn * 128 * BK;
+  const uint8_t* S = st + kScaleOff + BM * 4 + wn * 128 * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f.b[j] = frag(B + 32 * j * BK, fo);
+    f.sb[j] = *reinterpret_cast<const int*>(S + 32 * j * 4 + fo.sc);
+  }
+}
+
+__device__ __forceinline__ uint32_t shr(int v, int sel) { return (uint32_t)v >> sel; }
+
+// MFMAs of A fragments i0, i0 + 1 against the 4 B fragments.
+__device__ __forceinline__ void mma_half(const Frags& f, v16f (&acc)[4][4], int i0) {
+#pragma unroll
+  for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, f.sb[j], 0,
+                                                                  f.sa[i]);
+}
+
+// The MFMA results are only consumed tiles later, so the compiler would sink
+// MFMAs below the step's waits and barrier; an empty asm that claims to update
+// the accumulators keeps each half in place.
+__device__ __forceinline__ void pin(v16f (&acc)[4][4], int i0) {
+#pragma unroll
+  for (int i = i0; i < i0 + 2; ++i)
+    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]));
+}
+
+__device__ __forceinline__ void zero_acc(v16f (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
+// Tile epilogue, staged through LDS so that every global store writes whole
+// 128-byte lines.  Each wave owns a quarter of an LDS stage, 32 rows x 272 B
+// (64 fp32 columns + 16 B of padding, which puts the 32 rows written by one
+// ds_write_b128 in distinct bank groups).  For each 32 x 64 part of its
+// 128 x 128 result, a wave writes the fp32 accumulators (straight from the
+// accumulator registers), reads them back 8 consecutive columns per lane,
+// converts, and stores 8 rows x 64 columns per instruction.  Rows and
+// columns outside the tile get out-of-range offsets and are dropped, so
+// every wave issues exactly kTileStores store instructions per tile.
+constexpr int kEpiPitch = 272;
+constexpr int kEpiSlice = 32 * kEpiPitch;
+static_assert(4 * kEpiSlice == kStageBytes, "the epilogue uses one LDS stage");
+
+template <bool kF32>
+constexpr int tile_stores() { return kF32 ? 64 : 32; }
+
+template <bool kF32>
+__device__ __forceinline__ void store_tile(const OutTile& o, const v16f (&acc)[4][4], int wm, int wn,
+                                           uint8_t* stage) {
+  typedef unsigned int v4u_ __attribute__((ext_vector_type(4)));
+  constexpr int kEs = kF32 ? 4 : 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* slice = stage + wave * kEpiSlice;
+  const int64_t pitch = o.ldc * kEs;  // bytes per output row, < 2^23 (checked on the host)
+  char* base = static_cast<char*>(o.out) + (o.m0 * o.ldc + o.n0) * kEs;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)(o.rows * pitch), 0x00020000);
+  const int wr = lane & 31, h = lane >> 5;      // write side: accumulator layout
+  const int rr = lane >> 3, c8 = lane & 7;      // read side: 8 lanes per row, 8 columns each
+  const int32_t cols = (int32_t)(o.n_end - o.n0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v16f& v = acc[i][2 * jp + jj];
+          *reinterpret_cast<float4*>(slice + wr * kEpiPitch + (32 * jj + 8 * q + 4 * h) * 4) =
+              make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = 8 * it + rr;
+        const float4 a = *reinterpret_cast<const float4*>(slice + row * kEpiPitch + 32 * c8);
+        const float4 b = *reinterpret_cast<const float4*>(slice + row * kEpiPitch + 32 * c8 + 16);
+        const int ml = wm * 128 + 32 * i + row;
+        const int col = wn * 128 + 64 * jp + 8 * c8;  // n_end % 32 == 0: the 8 columns are all in or all out
+        const uint32_t voff =
+            (ml < o.rows) & (col < cols) ? (uint32_t)ml * (uint32_t)pitch + (uint32_t)(col * kEs) : kOob;
+        if (kF32) {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, a), r, voff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, b), r, voff + 16, 0, 0);
+        } else {
+          const v4u_ d = {bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y), bf16x2_rne(b.z, b.w)};
+          __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, 0);
+        }
+      }
+    }
+  }
+}
+
+// Compute-side cursor.
+struct Cursor {
+  OutTile t;
+  int64_t L;
+  int32_t s;      // k step within the tile (padding steps included)
+};
+
+// After the last step of a tile: store it and move on to the next tile with k
+// steps, storing exact zeros for tiles without any (wgrad of an empty group).
+// Returns false when the workgroup has no tiles left.
+//
+// Vector memory operations complete in issue order, stores included, and
+// every tile store issues exactly tile_stores() instructions per wave.  So
+// the two mid-step waits right after a tile store have at least that many
+// more younger operations behind the loads they wait for (see kVmAfter).
+// The epilogue stages through LDS stage 3, which the next step's loads
+// overwrite: a barrier after it keeps every wave's reads ahead of them.
+template <bool kF32, bool kWgrad>
+__device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad>& w, v16f (&acc)[4][4], int wm, int wn,
+                                            uint8_t* st3) {
+  store_tile<kF32>(c.t, acc, wm, wn, st3);
+  zero_acc(acc);
+  c.s = 0;
+  bool more = true;
+  while (true) {
+    c.L += w.stride;
+    if (c.L >= w.L_end) {
+      more = false;
+      break;
+    }
+    c.t = out_tile<kWgrad>(w.p, w.at(c.L));
+    if (c.t.steps > 0) break;
+    store_tile<kF32>(c.t, acc, wm, wn, st3);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  return more;
+}
+
+// Wait until the own loads of stage s+1 are complete (kVm younger vector
+// memory operations may stay in flight), then a workgroup barrier.  The
+// barrier is a bare s_barrier: the fence of __syncthreads would also wait
+// for the loads of the later stages.  Compiler-level memory clobbers keep
+// LDS accesses from moving across it.
+template <int kVm>
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kVm));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One k step on stage CUR.  On entry `cur` holds the step's B fragments and
+// A fragments 0, 1 (read during the previous step); A fragments 2, 3 are read
+// during the first half.  The loads of the step three ahead go to stage
+// (CUR + 3) % 4, which every wave finished reading before the previous
+// step's barrier; after this step's barrier the B and first two A fragments
+// of the next step are read from stage (CUR + 1) % 4 into `nxt`.
+//
+// The step is written as 16 slots, one MFMA each, with the loads and LDS
+// reads spread over them; scheduling fences between slots keep that order.
+template <int CUR, int kVm, bool kWgrad>
+__device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3, Frags& cur, Frags& nxt,
+                                       v16f (&acc)[4][4], Loader& ld, const LaneLoads& ll, Cursor& c,
+                                       const Walk<kWgrad>& w, int wm, int wn, int64_t pa, int64_t pb,
+                                       const FragOff& fo) {
+  uint8_t* const nst = CUR == 0 ? s1 : CUR == 1 ? s2 : CUR == 2 ? s3 : s0;   // stage of step s+1
+  uint8_t* const lst = CUR == 0 ? s3 : CUR == 1 ? s0 : CUR == 2 ? s1 : s2;   // stage of step s+3
+  uint8_t* const cst = CUR == 0 ? s0 : CUR == 1 ? s1 : CUR == 2 ? s2 : s3;   // stage of step s
+  const int h = (threadIdx.x >> 5) & 1;
+  // the step's scale bytes: byte 2 * (k step parity) + h of the panel dword
+  const int sel = 8 * (2 * (c.s & 1) + h);
+  const LoadPlan pl = plan_loads(ld, ll, lst, pa, pb);
+  const uint8_t* A = cst + wm * 128 * BK;
+  const uint8_t* SA = cst + kScaleOff + wm * 128 * 4;
+  const uint8_t* nA = nst + wm * 128 * BK;
+  const uint8_t* nSA = nst + kScaleOff + wm * 128 * 4;
+  const uint8_t* nB = nst + kCodeBytes + wn * 128 * BK;
+  const uint8_t* nSB = nst + kScaleOff + BM * 4 + wn * 128 * 4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cur.sb[j] = (int)shr(cur.sb[j], sel);
+  cur.sa[0] = (int)shr(cur.sa[0], sel);
+  cur.sa[1] = (int)shr(cur.sa[1], sel);
   __builtin_amdgcn_sched_barrier(0);
+#define MX_MFMA(i, j)                                                                                        \
+  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0, cur.sb[j], \
+                                                              0, cur.sa[i]);
+#define MX_FENCE __builtin_amdgcn_sched_barrier(0);
+  // first half: MFMAs of A fragments 0, 1; loads 0..4; A fragments 2, 3
+  MX_MFMA(0, 0) load_n(pl, 0); cur.a[2] = frag(A + 64 * BK, fo);                      MX_FENCE
+  MX_MFMA(0, 1) load_n(pl, 1); cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc); MX_FENCE
+  MX_MFMA(0, 2) load_n(pl, 2); cur.a[3] = frag(A + 96 * BK, fo);                      MX_FENCE
+  MX_MFMA(0, 3) load_n(pl, 3); cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc); MX_FENCE
+  MX_MFMA(1, 0) load_n(pl, 4);                                                        MX_FENCE
+  MX_MFMA(1, 1)                                                                       MX_FENCE
+  MX_MFMA(1, 2)                                                                       MX_FENCE
+  MX_MFMA(1, 3)                                                                       MX_FENCE
+  pin(acc, 0);
+  // stage s+1 complete: own loads, then everyone's
+  stage_barrier<kVm>();
+  MX_FENCE
+  cur.sa[2] = (int)shr(cur.sa[2], sel);
+  cur.sa[3] = (int)shr(cur.sa[3], sel);
+  // second half: MFMAs of A fragments 2, 3; loads 5..9; the next step's B
+  // fragments and A fragments 0, 1
+  MX_MFMA(2, 0) load_n(pl, 5); nxt.b[0] = frag(nB, fo);            nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc);       MX_FENCE
+  MX_MFMA(2, 1) load_n(pl, 6); nxt.b[1] = frag(nB + 32 * BK, fo);  nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc); MX_FENCE
+  MX_MFMA(2, 2) load_n(pl, 7); nxt.b[2] = frag(nB + 64 * BK, fo);  nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc); MX_FENCE
+  MX_MFMA(2, 3) load_n(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo);  nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc); MX_FENCE
+  MX_MFMA(3, 0) load_n(pl, 9); nxt.a[0] = frag(nA, fo);            nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc);       MX_FENCE
+  MX_MFMA(3, 1)                nxt.a[1] = frag(nA + 32 * BK, fo);  nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc); MX_FENCE
+  MX_MFMA(3, 2)                                                                                                               MX_FENCE
+  MX_MFMA(3, 3)                                                                                                               MX_FENCE
+#undef MX_MFMA
+#undef MX_FENCE
+  pin(acc, 2);
+  // the next step's fragments are in registers before any wave can pass the
+  // next barrier and start overwriting their stage
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+  ++ld.s;
+  loader_seek<kWgrad>(ld, w);
+  ++c.s;
 }
 
 // Persistent workgroup: one per CU.  Logical tiles are split into 8 contiguous
 // ranges, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an
-// XCD walk their range round robin.  The first k stage of the next tile is
-// loaded during the last k step of the current one, so tile changes cost no
-// exposed load latency and the epilogue stores overlap the next loads.
+// XCD walk their range round robin.
 template <bool kF32, bool kWgrad>
-__global__ void __launch_bounds__(kThreads) k_gemm(RowsProblem p, const int32_t* __restrict__ offsets, int32_t E) {
+__global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __restrict__ offsets, int32_t E) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
   __shared__ Sched sc;
   const int64_t m_tiles = (p.N + BM - 1) / BM;  // wgrad only
   const int64_t n_tiles = kWgrad ? (p.K + BN - 1) / BN : (p.N + BN - 1) / BN;
   build_schedule(sc, offsets, E, p.m_cap, kWgrad ? 0 : (int32_t)n_tiles, kWgrad);
   const int64_t total = kWgrad ? (int64_t)E * m_tiles * n_tiles : (int64_t)uni(sc.tiles_before[E]);
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  const int64_t ctas_per_xcd = gridDim.x / kXcds;
   const int64_t x = blockIdx.x % kXcds;
   const int64_t L_end = (x + 1) * per_xcd < total ? (x + 1) * per_xcd : total;
-  int64_t L = x * per_xcd + blockIdx.x / kXcds;
-  if (L >= L_end) return;
-  const TileGen<kWgrad> gen{p, sc, E, m_tiles, n_tiles};
+  const int64_t L0 = x * per_xcd + blockIdx.x / kXcds;
+  if (L0 >= L_end) return;
+  const Walk<kWgrad> w{p, sc, E, m_tiles, n_tiles, (int64_t)(gridDim.x / kXcds), L_end};
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  v4f acc[8][8];
-  zero_acc(acc);
-  Tile cur = gen(L);
-  int buf = 0;  // stage holding the current tile's first k window
-  bool staged = false;
-  while (true) {
-    if (cur.steps > 0 && !staged) {
-      uint8_t* st = buf ? st1 : st0;
-      const StageLoad sl{cur.A, cur.B, st, cur.k_begin, cur.k_lo, cur.k_hi, true};
-      issue_stage(sl);
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int64_t Ln = L + ctas_per_xcd;
-    const bool has_next = Ln < L_end;
-    staged = false;
-    int s = 0;
-    if (buf && s < cur.steps) k_step<1>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
-    while (s + 1 < cur.steps) {
-      k_step<0>(st0, st1, cur, s, has_next, Ln, gen, staged, acc, wm, wn);
-      k_step<1>(st0, st1, cur, s + 1, has_next, Ln, gen, staged, acc, wm, wn);
-      s += 2;
-    }
-    if (s < cur.steps) k_step<0>(st0, st1, cur, s++, has_next, Ln, gen, staged, acc, wm, wn);
-    buf = (buf + cur.steps) & 1;
-    store_tile<kF32>(cur.out, cur.ldc, cur.m0, cur.A.rows, cur.n0, cur.n_end, acc, wm, wn);
-    zero_acc(acc);
-    if (!has_next) break;
-    cur = gen(Ln);
-    L = Ln;
+  const int lane = threadIdx.x & 63;
+  const int64_t ldb = kWgrad ? p.m_cap : p.K;
+  const int64_t pa = kWgrad ? 4 * p.N : 4 * p.m_cap;
+  const int64_t pb = kWgrad ? 4 * p.K : 4 * (int64_t)E * p.N;
+  LaneLoads ll;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (4 * wave + i) + (lane >> 2);
+    const int ch = (lane & 3) ^ swz(row);
+    ll.voff[i] = (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)ch;
+    ll.kc[i] = 16 * ch;
   }
+  ll.srow = 64 * wave + lane;
+  v16f acc[4][4];
+  zero_acc(acc);
+  // compute cursor: leading tiles without k steps are stored as zeros
+  Cursor c;
+  c.L = L0;
+  c.s = 0;
+  c.t = out_tile<kWgrad>(p, w.at(L0));
+  while (c.t.steps == 0) {
+    store_tile<kF32>(c.t, acc, wm, wn, st3);
+    c.L += w.stride;
+    if (c.L >= L_end) return;
+    c.t = out_tile<kWgrad>(p, w.at(c.L));
+  }
+  // loader: starts at the same tile; the prologue fills stages 0..2
+  Loader ld;
+  ld.L = c.L;
+  ld.t = load_tile<kWgrad>(p, w.at(c.L), E);
+  ld.s = 0;
+  ld.valid = true;
+  issue_all(plan_loads(ld, ll, st0, pa, pb));
+  ++ld.s;
+  loader_seek<kWgrad>(ld, w);
+  issue_all(plan_loads(ld, ll, st1, pa, pb));
+  ++ld.s;
+  loader_seek<kWgrad>(ld, w);
+  issue_all(plan_loads(ld, ll, st2, pa, pb));
+  ++ld.s;
+  loader_seek<kWgrad>(ld, w);
+  // drain the prologue: the first two steps wait with vmcnt(63)
+  stage_barrier<0>();
+  const FragOff fo = frag_off();
+  Frags fa, fb;
+  read_b(st0, fa, wn, fo);
+  read_a(st0, fa, wm, 0, 2, fo);
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // Steady state: stage s+1 is waited for with kVmem + kVmemFirst younger
+  // operations in flight (the loads of s+2 and the first part of s+3).  The
+  // first two steps of a tile follow a tile store (or the drained prologue):
+  // the tile's stores add tile_stores() younger operations, see finish_tile.
+  constexpr int kSteady = kVmem + kVmemFirst;
+  constexpr int kVmAfter = kSteady + tile_stores<kF32>() < 63 ? kSteady + tile_stores<kF32>() : 63;
+  do {
+    k_step<0, kVmAfter, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, kVmAfter, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<2, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<3, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    while (c.s < c.t.steps) {
+      k_step<0, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<2, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<3, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    }
+  } while (finish_tile<kF32, kWgrad>(c, w, acc, wm, wn, st3));
+  // loads past the last tile may still be writing LDS
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 template <bool kF32, bool kWgrad>
-void launch(int ctas, hipStream_t st, const RowsProblem& p, const int32_t* off, int32_t E) {
+void launch(int ctas, hipStream_t st, const Problem& p, const int32_t* off, int32_t E) {
   hipLaunchKernelGGL((k_gemm<kF32, kWgrad>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
 }
 
 template <bool kWgrad>
-int launch_any(const RowsProblem& p, const int32_t* off, int32_t E, hipStream_t st) {
+int launch_any(const Problem& p, const int32_t* off, int32_t E, hipStream_t st) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MX_EHIP;
@@ -511,7 +805,8 @@ static int gemm_rows(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
   if (((m_cap + BM - 1) / BM + E) * ((N + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
   const int64_t panels = (K + 127) / 128;  // scale spans addressed with 32-bit offsets
   if (panels * 4 * m_cap >= (1ll << 31) || panels * 4 * (int64_t)E * N >= (1ll << 31)) return MX_EINVAL;
-  const RowsProblem p{a_q, a_s, b_q, b_s, m_cap, N, K, out, out_dtype == MX_OUT_F32};
+  if (N >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x N x 4 bytes < 2^31
+  const Problem p{a_q, a_s, b_q, b_s, m_cap, N, K, out, out_dtype == MX_OUT_F32};
   return launch_any<false>(p, offsets, E, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -542,6 +837,7 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
   if ((int64_t)num_groups * ((n + BM - 1) / BM) * ((k + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
   const int64_t panels = (m_cap + 127) / 128;
   if (panels * 4 * n >= (1ll << 31) || panels * 4 * k >= (1ll << 31)) return MX_EINVAL;
-  const RowsProblem p{dyt_q, dyt_s, xt_q, xt_s, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
+  if (k >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x k x 4 bytes < 2^31
+  const Problem p{dyt_q, dyt_s, xt_q, xt_s, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
   return launch_any<true>(p, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
 }
