@@ -102,3 +102,36 @@ def check(gpu, C, S, h_fn=None, out_bf16=False):
         "max_err_over_S": float(ratio.max()) if ratio.size else 0.0,
         "first_fail": int(fail_idx[final_fail][0]) if final_fail.any() else -1,
     }
+
+
+# --------------------------------------------------------------------------
+# Element-wise glue (SwiGLU and its backward, the weighted combine)
+# --------------------------------------------------------------------------
+# These are a handful of fp32 operations per element (an exponential, a
+# reciprocal, a few products and sums, or k <= 8 fused multiply-adds), each
+# within one or two fp32 ulps of the exact result, followed by one bf16
+# rounding.  The rule: a bf16 result y passes when
+#     |y - exact| <= ulp_bf16(y) / 2 + GLUE_REL * S
+# with S the magnitude sum of the terms the result is built from (|A| for
+# SwiGLU, the sums returned by oracle.glue for its backward and the combine).
+# GLUE_REL = 2^-20 is 16 fp32 ulps, twice the sum of the per-operation bounds.
+GLUE_REL = 2.0 ** -20
+
+
+def check_bf16_elementwise(gpu_bits, exact, S, rel=GLUE_REL):
+    g = mxfp8.bf16_to_f64(np.asarray(gpu_bits, dtype=np.uint16).ravel())
+    C = np.asarray(exact, dtype=np.float64).ravel()
+    S = np.asarray(S, dtype=np.float64).ravel()
+    err = np.abs(g - C)
+    bound = 0.5 * bf16_ulp(np.asarray(gpu_bits, dtype=np.uint16).ravel()) + rel * S
+    bad = ~(err <= bound)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(bound > 0, err / bound, np.where(err > 0, np.inf, 0.0))
+    return {
+        "ok": bool(not bad.any()),
+        "n": int(C.size),
+        "fail": int(bad.sum()),
+        "max_err_over_bound": float(ratio.max()) if ratio.size else 0.0,
+        "first_fail": int(np.nonzero(bad)[0][0]) if bad.any() else -1,
+        "exact_rne": int(np.sum(np.asarray(gpu_bits, dtype=np.uint16).ravel() == mxfp8.f64_to_bf16(C))),
+    }
