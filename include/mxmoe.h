@@ -164,6 +164,75 @@ int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s, const uint
                           const int32_t* group_offsets, int32_t num_groups, int64_t m_cap, int64_t n, int64_t k,
                           void* dw, int32_t out_dtype, mx_stream_t stream);
 
+/*
+ * SwiGLU glue of the expert FFN with the requantize of its result fused in.
+ * The expert computation stays in MXFP8 between the GEMMs (digest "Key
+ * Questions Answered"; PR #3203 "Next steps": the grouped GEMM takes
+ * pre-quantized operands), so the activation goes straight from the gate/up
+ * GEMM output to the MX operands of the down GEMM (rowwise, along F) and of
+ * its wgrad (columnwise, along the rows).
+ *
+ *   h      bf16 [rows, 2F]: gate g in columns [0, F), up u in [F, 2F)
+ *   a      optional bf16 [rows, F]: A = RNE_bf16(silu(g) * u), silu(g) =
+ *          g / (1 + e^-g), computed in fp32
+ *   row_q/row_s  rowwise MX of A: codes [rows, F], scales [rows, F]; or NULL
+ *   col_q/col_s  columnwise MX of A stored transposed: codes [F, rows],
+ *          scales [F, rows]; or NULL (then rows % 32 == 0 is not required)
+ * The MX results are exactly the quantize of the bf16 A (whether or not a is
+ * written).  Requires F % 32 == 0, rows % 32 == 0 with a columnwise output,
+ * at least one output; h 16-byte aligned.  Rows of zeros (the pad rows of a
+ * grouped buffer) give zero codes and zero scales.
+ */
+int mx_swiglu_quantize(const uint16_t* h, int64_t rows, int64_t F, uint16_t* a, uint8_t* row_q, uint8_t* row_s,
+                       uint8_t* col_q, uint8_t* col_s, mx_stream_t stream);
+
+/*
+ * SwiGLU backward with the requantize of dH fused in (the dgrad operand of
+ * the gate/up GEMM rowwise along 2F, its wgrad operand columnwise).
+ *   h   bf16 [rows, 2F] (as in the forward), da bf16 [rows, F]
+ *   dh  optional bf16 [rows, 2F] = [dg | du], fp32 math, one RNE rounding:
+ *       dg = dA u s (1 + g (1 - s)), du = dA silu(g), s = 1 / (1 + e^-g)
+ *   row_q/row_s  rowwise MX of dH [rows, 2F]; col_q/col_s columnwise MX of dH
+ *       stored transposed [2F, rows]; either pair may be NULL.
+ * Same requirements as mx_swiglu_quantize.
+ */
+int mx_swiglu_bwd_quantize(const uint16_t* h, const uint16_t* da, int64_t rows, int64_t F, uint16_t* dh,
+                           uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, uint8_t* col_s, mx_stream_t stream);
+
+/*
+ * Weighted unpermute-combine (the step after the down GEMM; the inverse of
+ * the MXFP8 token shuffle of PR #3203 "Next steps").
+ *   y        bf16 [y_rows, H]: permuted rows (e.g. the down GEMM output)
+ *   dst_row  int32 [tokens * topk] from mx_permute
+ *   weights  fp32 [tokens, topk], or NULL for all ones (then this is the
+ *            backward of the permute: dX[t] = sum_j dX_perm[dst_row[t k + j]])
+ *   out      bf16 [tokens, H]: out[t] = RNE_bf16(sum_j w[t,j] y[dst_row[t k + j]]),
+ *            accumulated in fp32 with fused multiply-adds, j ascending
+ * A dst_row entry outside [0, y_rows) contributes nothing.  Requires
+ * H % 32 == 0, topk >= 1; y and out 16-byte aligned.
+ */
+int mx_combine(const uint16_t* y, int64_t y_rows, int64_t H, const int32_t* dst_row, const float* weights,
+               int64_t tokens, int32_t topk, uint16_t* out, mx_stream_t stream);
+
+/*
+ * Backward of the weighted combine with the quantize of the permuted
+ * gradient fused in (the dgrad operand of the down GEMM rowwise along H,
+ * its wgrad operand columnwise along the rows).
+ *   dout     bf16 [tokens, H]; weights fp32 [tokens, topk]
+ *   dst_row  int32 [tokens * topk], src_row int32 [rows] from mx_permute
+ *   dy       optional bf16 [rows, H]: dY[dst_row[i]] = RNE_bf16(fl32(w[i] *
+ *            dOut[i / topk])) (one fp32 product); rows no pair maps to are 0
+ *   row_q/row_s  rowwise MX of dY [rows, H]; col_q/col_s columnwise MX of dY
+ *            stored transposed [H, rows]; either pair may be NULL.
+ * Row r finds its pair as the j with dst_row[src_row[r] * topk + j] == r; a
+ * row without one is zero.  Requires H % 32 == 0, topk >= 1, rows % 32 == 0
+ * with a columnwise output; dout 16-byte aligned.  With tokens == 0, dout,
+ * weights and dst_row may be NULL (every row is zero).
+ */
+int mx_combine_bwd_quantize(const uint16_t* dout, const float* weights, const int32_t* dst_row,
+                            const int32_t* src_row, int64_t tokens, int32_t topk, int64_t rows, int64_t H, uint16_t* dy,
+                            uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, uint8_t* col_s, mx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

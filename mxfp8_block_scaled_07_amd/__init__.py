@@ -31,6 +31,11 @@ _SIGNATURES = {
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "mx_swiglu_quantize": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mx_swiglu_bwd_quantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mx_combine": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _i32, _vp, _vp]),
+    "mx_combine_bwd_quantize": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
+                                               _vp]),
 }
 
 
@@ -106,6 +111,28 @@ def mx_grouped_gemm_wgrad(dyt_q, dyt_s, xt_q, xt_s, group_offsets, num_groups, m
                                        n, k, _p(dw), out_dtype, _s(stream)), "mx_grouped_gemm_wgrad")
 
 
+def mx_swiglu_quantize(h, rows, F, a, row_q, row_s, col_q, col_s, stream=None):
+    _check(lib().mx_swiglu_quantize(_p(h), rows, F, _p(a), _p(row_q), _p(row_s), _p(col_q), _p(col_s), _s(stream)),
+           "mx_swiglu_quantize")
+
+
+def mx_swiglu_bwd_quantize(h, da, rows, F, dh, row_q, row_s, col_q, col_s, stream=None):
+    _check(lib().mx_swiglu_bwd_quantize(_p(h), _p(da), rows, F, _p(dh), _p(row_q), _p(row_s), _p(col_q), _p(col_s),
+                                        _s(stream)), "mx_swiglu_bwd_quantize")
+
+
+def mx_combine(y, y_rows, H, dst_row, weights, tokens, topk, out, stream=None):
+    _check(lib().mx_combine(_p(y), y_rows, H, _p(dst_row), _p(weights), tokens, topk, _p(out), _s(stream)),
+           "mx_combine")
+
+
+def mx_combine_bwd_quantize(dout, weights, dst_row, src_row, tokens, topk, rows, H, dy, row_q, row_s, col_q, col_s,
+                            stream=None):
+    _check(lib().mx_combine_bwd_quantize(_p(dout), _p(weights), _p(dst_row), _p(src_row), tokens, topk, rows, H,
+                                         _p(dy), _p(row_q), _p(row_s), _p(col_q), _p(col_s), _s(stream)),
+           "mx_combine_bwd_quantize")
+
+
 # --- allocating helpers ----------------------------------------------------
 def scale_shape(rows, cols):
     """Shape of the scale bytes of an MX tensor with ``rows`` rows (batch
@@ -160,3 +187,58 @@ def permute(q, s, expert_ids, num_experts, capacity_rows=None, stream=None):
     ws = torch.empty(max(wsb, 4), dtype=torch.uint8, device=dev)
     mx_permute(q, s, tokens, cols, expert_ids, topk, num_experts, cap, q_out, s_out, off, dst, src, ws, wsb, stream)
     return q_out, s_out, off, dst, src
+
+
+def _mx_pair(rows, cols, dev, want):
+    import torch
+    if not want:
+        return None, None
+    return (torch.empty((rows, cols), dtype=torch.uint8, device=dev),
+            torch.empty(scale_shape(rows, cols), dtype=torch.uint8, device=dev))
+
+
+def swiglu_quantize(h, rowwise=True, colwise=True, want_bf16=False, stream=None):
+    """h: bf16 [rows, 2F].  Returns (a_bf16, row_q, row_s, col_q, col_s)."""
+    import torch
+    rows, F = h.shape[0], h.shape[1] // 2
+    a = torch.empty((rows, F), dtype=torch.bfloat16, device=h.device) if want_bf16 else None
+    rq, rs = _mx_pair(rows, F, h.device, rowwise)
+    cq, cs = _mx_pair(F, rows, h.device, colwise)
+    if rows:   # an empty input has nothing to compute (its tensors have no storage)
+        mx_swiglu_quantize(h, rows, F, a, rq, rs, cq, cs, stream)
+    return a, rq, rs, cq, cs
+
+
+def swiglu_bwd_quantize(h, da, rowwise=True, colwise=True, want_bf16=False, stream=None):
+    """h: bf16 [rows, 2F], da: bf16 [rows, F].  Returns (dh_bf16, row_q, row_s, col_q, col_s)."""
+    import torch
+    rows, F = h.shape[0], h.shape[1] // 2
+    dh = torch.empty((rows, 2 * F), dtype=torch.bfloat16, device=h.device) if want_bf16 else None
+    rq, rs = _mx_pair(rows, 2 * F, h.device, rowwise)
+    cq, cs = _mx_pair(2 * F, rows, h.device, colwise)
+    if rows:
+        mx_swiglu_bwd_quantize(h, da, rows, F, dh, rq, rs, cq, cs, stream)
+    return dh, rq, rs, cq, cs
+
+
+def combine(y, dst_row, weights, tokens, topk, stream=None):
+    """y: bf16 [rows, H] permuted rows; weights fp32 [tokens, topk] or None.  Returns bf16 [tokens, H]."""
+    import torch
+    out = torch.empty((tokens, y.shape[1]), dtype=torch.bfloat16, device=y.device)
+    if tokens:
+        mx_combine(y, y.shape[0], y.shape[1], dst_row, weights, tokens, topk, out, stream)
+    return out
+
+
+def combine_bwd_quantize(dout, weights, dst_row, src_row, topk, rows, rowwise=True, colwise=True, want_bf16=False,
+                         stream=None):
+    """dout: bf16 [tokens, H].  Returns (dy_bf16, row_q, row_s, col_q, col_s) of the permuted gradient [rows, H]."""
+    import torch
+    tokens, H = dout.shape
+    dy = torch.empty((rows, H), dtype=torch.bfloat16, device=dout.device) if want_bf16 else None
+    rq, rs = _mx_pair(rows, H, dout.device, rowwise)
+    cq, cs = _mx_pair(H, rows, dout.device, colwise)
+    if rows:
+        mx_combine_bwd_quantize(dout if tokens else None, weights if tokens else None, dst_row if tokens else None,
+                                src_row, tokens, topk, rows, H, dy, rq, rs, cq, cs, stream)
+    return dy, rq, rs, cq, cs

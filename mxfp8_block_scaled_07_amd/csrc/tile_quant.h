@@ -1,0 +1,221 @@
+// The 128 x 128 tile quantizer behind every MXFP8 quantize of the library:
+// the plain quantize, the quantize of gathered (permuted) rows, and the
+// quantizes fused into the SwiGLU and combine glue.  A tile of bf16 values
+// is produced by a source (a load, a gather, or an element-wise function of
+// other tensors), and written as any of: its rowwise MX codes and scales, its
+// columnwise MX codes and scales (transposed), and the bf16 values
+// themselves.
+//
+// MX rule (digest "Key Questions Answered": one scale per fine-grained
+// sub-block; pytorch/ao PR #3203 stacked list: MXFP8 quantization kernel):
+// per 32-element block, scale byte = floor(log2 amax) - 8 clamped to the
+// E8M0 range, codes = E4M3 of x / 2^scale, RNE, saturating.
+//
+// Work split (256 threads = 4 waves).  Thread (wave w, lane = 16 ry + ch)
+// owns the 8 consecutive tile rows 32w + 8ry .. +7 at the 8 columns
+// 8ch .. 8ch+7: eight 16-byte loads, each wave instruction covering four
+// full 256-byte tile rows.
+// * Rowwise: the 4 lanes of a quad hold one 32-column block of a row; the
+//   amax is reduced with DPP quad permutes.  The 4 scale bytes of a row (one
+//   128-column panel) are merged into one dword with DPP row shifts and
+//   stored by one lane, so panel dwords are whole.
+// * Columnwise: the thread transposes its 8 x 8 block in registers and
+//   writes 8 columns x 16 bytes into an LDS tile kept column-major (a column
+//   = 128 rows = 256 bytes = 16 slots of 16 bytes; slot s of column c sits
+//   at slot s ^ ((c ^ (c >> 3)) & 15), which keeps both the write and the
+//   read pattern spread over all banks).  Thread (column c, half h) then
+//   reads rows 64h .. 64h+63 of column c, quantizes its two 32-row blocks,
+//   writes 64 contiguous code bytes and the two scale bytes (a 16-bit store;
+//   the 4 scale bytes of a column tile form one panel dword).
+#pragma once
+
+#include "mx_device.h"
+
+namespace mx {
+
+constexpr int kTq = 128;
+constexpr int kTqThreads = 256;
+
+struct TqShape {
+  int64_t rows_out;  // output rows per batch item
+  int64_t cols;      // output columns
+  int32_t n_tr;      // row tiles per batch item
+  int32_t n_tc;      // column tiles
+  int32_t batch;
+};
+
+struct TqOut {
+  uint8_t* row_q;  // rowwise codes [batch * rows_out, cols] (or null)
+  uint8_t* row_s;  // rowwise scales, panel layout over batch * rows_out rows
+  uint8_t* col_q;  // columnwise codes [batch, cols, rows_out] (or null)
+  uint8_t* col_s;  // columnwise scales, panel layout over batch * cols rows
+  uint16_t* y;     // bf16 values [batch * rows_out, cols] (or null)
+};
+
+__device__ __forceinline__ uint32_t tq_comp(const uint4& v, int k) {
+  return k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ int tq_swz(int c) { return (c ^ (c >> 3)) & 15; }
+
+__device__ __forceinline__ uint32_t dpp_row_shr(uint32_t v, int n4or8) {
+  return n4or8 == 4 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true)
+                    : (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ uint32_t amax8(const uint4& v) {
+  const v2u16 m = vmax(vmax(absbits(v.x), absbits(v.y)), vmax(absbits(v.z), absbits(v.w)));
+  return hmax(m);
+}
+
+// Source concept:
+//   struct Table;                          LDS table filled once per tile (may be empty)
+//   static constexpr bool kTable;          whether fill_table must run
+//   __device__ void fill_table(Table&, int64_t b, int64_t r0, int64_t rows_out) const;
+//   struct Row { bool ok; ... };
+//   __device__ Row row(const Table&, int64_t b, int64_t r, int local_r, bool in_range) const;
+//   struct Raw;
+//   __device__ Raw fetch(const Row&, int64_t col) const;     only when row.ok
+//   __device__ uint4 finish(const Raw&, const Row&, int64_t col) const;   8 bf16
+// Rows or columns outside the output, and rows the source marks !ok, are
+// zero: they raise no amax and produce zero codes (and zero pad scales).
+template <class Src, bool kRow, bool kCol, bool kY>
+__global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const TqShape sh, const TqOut o) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kCol ? kTq * kTq * 2 : 16];
+  __shared__ typename Src::Table table;
+  uint32_t idx = blockIdx.x;
+  const int32_t tc = (int32_t)(idx % (uint32_t)sh.n_tc);
+  idx /= (uint32_t)sh.n_tc;
+  const int32_t tr = (int32_t)(idx % (uint32_t)sh.n_tr);
+  const int32_t b = (int32_t)(idx / (uint32_t)sh.n_tr);
+  const int64_t r0 = (int64_t)tr * kTq, c0 = (int64_t)tc * kTq;
+  const int t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int ch = lane & 15, ry = lane >> 4;
+  const int lr0 = 32 * w + 8 * ry;
+  const int64_t col = c0 + 8 * ch;
+  const bool col_ok = col < sh.cols;  // cols % 32 == 0: a chunk is all in or all out
+  if (Src::kTable) {
+    src.fill_table(table, b, r0, sh.rows_out);
+    __syncthreads();
+  }
+
+  uint4 v[8];
+  {
+    typename Src::Row rw[8];
+    typename Src::Raw raw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + lr0 + i;
+      rw[i] = src.row(table, b, r, lr0 + i, r < sh.rows_out && col_ok);
+      if (rw[i].ok) raw[i] = src.fetch(rw[i], col);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = rw[i].ok ? src.finish(raw[i], rw[i], col) : make_uint4(0, 0, 0, 0);
+  }
+
+  if (kRow || kY) {
+    const int64_t R = (int64_t)sh.batch * sh.rows_out;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r0 + lr0 + i;
+      const bool r_ok = r < sh.rows_out;
+      const int64_t orow = (int64_t)b * sh.rows_out + r;
+      if (kY && r_ok && col_ok) *reinterpret_cast<uint4*>(o.y + orow * sh.cols + col) = v[i];
+      if (kRow) {
+        const uint32_t sb = scale_byte_from_amax(quad_max(amax8(v[i])));
+        const float sc = e8m0_to_f32(sb);
+        if (r_ok && col_ok)
+          *reinterpret_cast<uint2*>(o.row_q + orow * sh.cols + col) =
+              make_uint2(cvt4_e4m3(v[i].x, v[i].y, sc), cvt4_e4m3(v[i].z, v[i].w, sc));
+        uint32_t d = sb << (8 * (ch >> 2));
+        d |= dpp_row_shr(d, 4);
+        d |= dpp_row_shr(d, 8);
+        if (r_ok && ch == 12) *reinterpret_cast<uint32_t*>(o.row_s + ((c0 >> 7) * R + orow) * 4) = d;
+      }
+    }
+  }
+
+  if (kCol) {
+    const int slot = lr0 >> 3;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int cc = 8 * ch + j;
+      const int k = j >> 1;
+      uint32_t d[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const uint32_t a = tq_comp(v[2 * p], k), bb = tq_comp(v[2 * p + 1], k);
+        d[p] = (j & 1) ? (a >> 16) | (bb & 0xFFFF0000u) : (a & 0xFFFFu) | (bb << 16);
+      }
+      *reinterpret_cast<uint4*>(lds + cc * 256 + 16 * (slot ^ tq_swz(cc))) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+    __syncthreads();
+    const int c = t >> 1, hf = t & 1;
+    const int64_t gc = c0 + c;
+    if (gc < sh.cols) {
+      uint32_t sbs = 0;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        uint4 q4[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          q4[s] = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((8 * hf + 4 * blk + s) ^ tq_swz(c)));
+        uint32_t m = 0;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t ms = amax8(q4[s]);
+          m = m > ms ? m : ms;
+        }
+        const uint32_t sb = scale_byte_from_amax(m);
+        const float sc = e8m0_to_f32(sb);
+        sbs |= sb << (8 * blk);
+        const int64_t gr = r0 + 64 * hf + 32 * blk;
+        if (gr < sh.rows_out) {
+          uint8_t* dst = o.col_q + ((int64_t)b * sh.cols + gc) * sh.rows_out + gr;
+          *reinterpret_cast<uint4*>(dst) = make_uint4(cvt4_e4m3(q4[0].x, q4[0].y, sc), cvt4_e4m3(q4[0].z, q4[0].w, sc),
+                                                      cvt4_e4m3(q4[1].x, q4[1].y, sc), cvt4_e4m3(q4[1].z, q4[1].w, sc));
+          *reinterpret_cast<uint4*>(dst + 16) =
+              make_uint4(cvt4_e4m3(q4[2].x, q4[2].y, sc), cvt4_e4m3(q4[2].z, q4[2].w, sc),
+                         cvt4_e4m3(q4[3].x, q4[3].y, sc), cvt4_e4m3(q4[3].z, q4[3].w, sc));
+        }
+      }
+      const int64_t C = (int64_t)sh.batch * sh.cols;
+      *reinterpret_cast<uint16_t*>(o.col_s + ((r0 >> 7) * C + (int64_t)b * sh.cols + gc) * 4 + 2 * hf) =
+          (uint16_t)sbs;
+    }
+  }
+}
+
+// Host side: the tile grid of a quantize, checked against its limits.
+inline bool tq_shape(int64_t batch, int64_t rows_out, int64_t cols, TqShape& sh, unsigned& grid) {
+  sh.rows_out = rows_out;
+  sh.cols = cols;
+  const int64_t ntr = (rows_out + kTq - 1) / kTq, ntc = (cols + kTq - 1) / kTq;
+  const int64_t n = batch * ntr * ntc;
+  if (n <= 0 || n > 0x7FFFFFFF || batch > 0x7FFFFFFF) return false;
+  sh.n_tr = (int32_t)ntr;
+  sh.n_tc = (int32_t)ntc;
+  sh.batch = (int32_t)batch;
+  grid = (unsigned)n;
+  return true;
+}
+
+// Launch k_tile_quant with the outputs the caller asked for (row and/or col
+// and/or the bf16 copy).  Returns the launch status.
+template <class Src>
+inline int tq_launch(const Src& src, const TqShape& sh, unsigned grid, const TqOut& o, hipStream_t st) {
+  const bool r = o.row_q != nullptr, c = o.col_q != nullptr, y = o.y != nullptr;
+  const dim3 g(grid), bl(kTqThreads);
+  if (r && c && y) hipLaunchKernelGGL((k_tile_quant<Src, true, true, true>), g, bl, 0, st, src, sh, o);
+  else if (r && c) hipLaunchKernelGGL((k_tile_quant<Src, true, true, false>), g, bl, 0, st, src, sh, o);
+  else if (r && y) hipLaunchKernelGGL((k_tile_quant<Src, true, false, true>), g, bl, 0, st, src, sh, o);
+  else if (r) hipLaunchKernelGGL((k_tile_quant<Src, true, false, false>), g, bl, 0, st, src, sh, o);
+  else if (c && y) hipLaunchKernelGGL((k_tile_quant<Src, false, true, true>), g, bl, 0, st, src, sh, o);
+  else if (c) hipLaunchKernelGGL((k_tile_quant<Src, false, true, false>), g, bl, 0, st, src, sh, o);
+  else if (y) hipLaunchKernelGGL((k_tile_quant<Src, false, false, true>), g, bl, 0, st, src, sh, o);
+  else return MX_EINVAL;
+  return launch_status();
+}
+
+}  // namespace mx

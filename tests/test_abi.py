@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"mx_quantize", "mx_dequantize", "mx_permute", "mx_permute_workspace_size",
                           "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
-                          "mx_status_string"}
+                          "mx_status_string", "mx_swiglu_quantize", "mx_swiglu_bwd_quantize", "mx_combine",
+                          "mx_combine_bwd_quantize"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -88,6 +89,46 @@ def test_gemm_validation(lib):
     w = lib.mx_grouped_gemm_wgrad
     assert w(P, P, P, P, P, 2, 48, 64, 64, P, 0, None) == mxa.MX_EINVAL        # m_cap % 32
     assert w(P, P, P, P, None, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL
+
+
+Q = ctypes.c_void_p(8)  # 8-byte aligned only: rejected where 16-byte loads or stores need alignment
+
+
+def test_quantize_alignment(lib):
+    q = lib.mx_quantize
+    assert q(Q, 1, 32, 32, None, 32, P, P, None, None, None) == mxa.MX_EINVAL             # x not 16-aligned
+    assert q(P, 1, 32, 32, None, 32, None, None, Q, P, None) == mxa.MX_EINVAL             # col codes
+    assert q(P, 1, 32, 32, None, 32, P, ctypes.c_void_p(18), None, None, None) == mxa.MX_EINVAL   # scales
+
+
+def test_swiglu_validation(lib):
+    f = lib.mx_swiglu_quantize
+    assert f(None, 64, 64, P, None, None, None, None, None) == mxa.MX_EINVAL             # h null
+    assert f(P, 64, 48, P, None, None, None, None, None) == mxa.MX_EINVAL                # F % 32
+    assert f(P, 64, 64, None, None, None, None, None, None) == mxa.MX_EINVAL             # no output
+    assert f(P, 40, 64, None, None, None, P, P, None) == mxa.MX_EINVAL                   # colwise rows % 32
+    assert f(P, 64, 64, None, P, None, None, None, None) == mxa.MX_EINVAL                # half a pair
+    assert f(Q, 64, 64, P, None, None, None, None, None) == mxa.MX_EINVAL                # h alignment
+    assert f(P, 0, 64, P, None, None, None, None, None) == mxa.MX_OK                     # empty
+    b = lib.mx_swiglu_bwd_quantize
+    assert b(P, None, 64, 64, P, None, None, None, None, None) == mxa.MX_EINVAL          # da null
+    assert b(P, P, 64, 16, P, None, None, None, None, None) == mxa.MX_EINVAL             # F % 32
+    assert b(P, P, 64, 64, None, None, None, None, None, None) == mxa.MX_EINVAL          # no output
+    assert b(P, P, 0, 64, P, None, None, None, None, None) == mxa.MX_OK
+
+
+def test_combine_validation(lib):
+    c = lib.mx_combine
+    assert c(None, 64, 64, P, P, 8, 2, P, None) == mxa.MX_EINVAL                         # y null
+    assert c(P, 64, 48, P, P, 8, 2, P, None) == mxa.MX_EINVAL                            # H % 32
+    assert c(P, 64, 64, P, P, 8, 0, P, None) == mxa.MX_EINVAL                            # topk 0
+    assert c(P, 64, 64, None, P, 8, 2, P, None) == mxa.MX_EINVAL                         # dst null
+    assert c(P, 64, 64, P, None, 0, 2, P, None) == mxa.MX_OK                             # no tokens
+    b = lib.mx_combine_bwd_quantize
+    assert b(P, None, P, P, 8, 2, 64, 64, P, None, None, None, None, None) == mxa.MX_EINVAL   # weights null
+    assert b(P, P, P, P, 8, 2, 40, 64, None, None, None, P, P, None) == mxa.MX_EINVAL        # colwise rows % 32
+    assert b(P, P, P, P, 8, 2, 64, 64, None, None, None, None, None, None) == mxa.MX_EINVAL  # no output
+    assert b(P, P, P, P, 8, 2, 0, 64, P, None, None, None, None, None) == mxa.MX_OK
 
 
 def test_python_binding_raises(lib):
