@@ -531,6 +531,11 @@ __device__ __forceinline__ void store_tile(const OutTile& o, const v16f (&acc)[4
           *reinterpret_cast<float4*>(slice + wr * kEpiPitch + (32 * jj + 8 * q + 4 * h) * 4) =
               make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
+      // The slice is exchanged between lanes of the wave.  The wave's LDS
+      // accesses execute in order, but the compiler reasons per lane: without
+      // this clobber it may reuse an earlier read of the same address or move
+      // a read across another lane's write.
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const int row = 8 * it + rr;
@@ -548,6 +553,7 @@ __device__ __forceinline__ void store_tile(const OutTile& o, const v16f (&acc)[4
           __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, 0);
         }
       }
+      asm volatile("" ::: "memory");
     }
   }
 }
