@@ -16,7 +16,9 @@ mean duration (HIP events on the launch stream, every timed step) and its
 throughput against the MI355X peak (MXFP8 dense 5.0 PFLOP/s, HBM 8 TB/s).
 ``roofline`` reports the dominant GEMM stage.  ``quantize_bandwidth`` times
 the fused rowwise+columnwise quantize and both dequantizes of a
-[16*8192, 5120] bf16 tensor.  ``cpu_baseline`` times the oracle on a bounded
+[16*8192, 5120] bf16 tensor.  ``swiglu_layer`` times the full SwiGLU expert
+FFN layer (64 experts, top-8, 32768 tokens, hidden 7168, ffn 2048) forward
+plus backward, stage by stage, including the SwiGLU and combine glue.  ``cpu_baseline`` times the oracle on a bounded
 sample (one expert's share of the step).
 """
 
@@ -185,6 +187,67 @@ def gpu_quantize_bandwidth(args):
     return out
 
 
+def gpu_swiglu_layer(args):
+    """The full SwiGLU expert FFN layer of the 64-expert top-8 workload (T=32768
+    tokens, hidden 7168, expert ffn 2048), forward plus backward, on seeded
+    synthetic inputs generated on the GPU: router logits N(0,1) -> top-8 and
+    softmax weights over the 8, X and dOut bf16 N(0,1), W1 [64, 4096, 7168] and
+    W2 [64, 7168, 2048] bf16 0.02*N(0,1).  Every stage is timed like the
+    headline step; the glue kernels (SwiGLU, combine and their backwards) are
+    reported against HBM bandwidth."""
+    import torch
+
+    from mxfp8_block_scaled_07_amd import moe
+
+    T, H, F, E, k = 32768, 7168, 2048, 64, 8
+    dev = "cuda:0"
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+
+    def normal_bf16(shape, std):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        flat = out.view(-1)
+        ch = 1 << 26               # chunked: keeps the fp32 temporary small
+        for i in range(0, flat.numel(), ch):
+            n = min(ch, flat.numel() - i)
+            flat[i:i + n] = (torch.randn(n, generator=g, device=dev) * std).to(torch.bfloat16)
+        return out
+
+    logits = torch.randn((T, E), generator=g, device=dev)
+    top = torch.topk(logits, k, dim=1)
+    ids = top.indices.to(torch.int32).contiguous()
+    weights = torch.softmax(top.values, dim=1).float().contiguous()
+    x = normal_bf16((T, H), 1.0)
+    dout = normal_bf16((T, H), 1.0)
+    w1 = normal_bf16((E, 2 * F, H), 0.02)
+    w2 = normal_bf16((E, H, F), 0.02)
+    b = moe.LayerBuffers(T, H, F, E, k, device=dev)
+    torch.cuda.synchronize()
+    steps = max(3, args.steps // 4)
+    step_ms, per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, ids, weights, dout),
+                                  moe.LAYER_STAGES, steps, 2)
+    work = moe.layer_work(T, H, F, E, k)
+    stages = {}
+    for n in moe.LAYER_STAGES:
+        ms = per[n]
+        if n in work["gemm_flops"]:
+            tf = work["gemm_flops"][n] / (ms * 1e-3) / 1e12
+            stages[n] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4)}
+        else:
+            gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
+            stages[n] = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+    flops = sum(work["gemm_flops"].values())
+    tf = flops / (step_ms * 1e-3) / 1e12
+    res = {"workload": "SwiGLU expert FFN layer fwd+bwd: T=32768 tokens, top-8 of E=64 experts (262144 routed "
+                       "rows), hidden 7168, expert ffn 2048, bf16 N(0,1) activations, 0.02*N(0,1) weights, "
+                       "MXFP8 GEMM operands, bf16 GEMM outputs",
+           "steps": steps, "ms_per_step": round(step_ms, 3), "gemm_tflop_per_step": round(flops / 1e12, 3),
+           "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4), "stages": stages}
+    del b, x, dout, w1, w2
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration():
     """A plain device-to-device copy of CALIB_BYTES, three launches: the
     reference the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
@@ -250,6 +313,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant-bench", action="store_true")
+    ap.add_argument("--no-layer", action="store_true", help="skip the SwiGLU expert FFN layer workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -269,6 +333,8 @@ def main():
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)
+    if not args.no_layer:
+        line["swiglu_layer"] = gpu_swiglu_layer(args)
     if args.copy_calibration:
         copy_calibration()
     if not args.no_cpu_baseline:

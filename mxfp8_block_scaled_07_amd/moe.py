@@ -21,8 +21,9 @@ combine backward writes); ``zero_pad_rows`` prepares such a tensor.
 
 import torch
 
-from . import (MX_OUT_BF16, MX_OUT_F32, mx_grouped_gemm_dgrad, mx_grouped_gemm_fwd, mx_grouped_gemm_wgrad,
-               mx_permute, mx_permute_workspace_size, mx_quantize, scale_shape)
+from . import (MX_OUT_BF16, MX_OUT_F32, mx_combine, mx_combine_bwd_quantize, mx_grouped_gemm_dgrad,
+               mx_grouped_gemm_fwd, mx_grouped_gemm_wgrad, mx_permute, mx_permute_workspace_size, mx_quantize,
+               mx_swiglu_bwd_quantize, mx_swiglu_quantize, scale_shape)
 
 STAGES = ("quant_x", "permute", "quant_w", "gemm_fwd", "quant_dy", "gemm_dgrad", "quant_xt", "gemm_wgrad")
 
@@ -112,5 +113,126 @@ def algorithmic_work(T, K, N, E, topk, m_real=None):
             "quant_w": rowcol_b(E * N, K),
             "quant_dy": rowcol_b(cap, N),
             "quant_xt": M * K * 2 + cap * K * (1 + 1 / 32) + 4 * cap,
+        },
+    }
+
+
+# ---------------------------------------------------------------------------
+# The SwiGLU expert FFN layer: gate/up GEMM -> SwiGLU -> down GEMM ->
+# weighted combine, forward and backward, every operand of every GEMM in
+# MXFP8.  W1 [E, 2F, H] holds the gate rows [0, F) and the up rows [F, 2F)
+# of each expert; W2 [E, H, F].
+# ---------------------------------------------------------------------------
+LAYER_STAGES = ("quant_x", "permute", "quant_w1", "gemm1_fwd", "swiglu", "quant_w2", "gemm2_fwd", "combine",
+                "combine_bwd", "gemm2_dgrad", "gemm2_wgrad", "swiglu_bwd", "gemm1_dgrad", "quant_xt",
+                "gemm1_wgrad", "unpermute_dx")
+
+
+class LayerBuffers:
+    """Device buffers of one SwiGLU expert FFN layer (T tokens, hidden H,
+    expert ffn F, E experts, top-k), allocated once.  Buffers that a kernel
+    reads over all capacity rows but a grouped GEMM only writes inside the
+    groups (h, da) start zeroed, so rows past the last group stay zero."""
+
+    def __init__(self, T, H, F, E, topk, device="cuda:0"):
+        self.T, self.H, self.F, self.E, self.topk = T, H, F, E, topk
+        self.cap = cap = -(-(T * topk + 31 * E) // 32) * 32
+        u8, i32, bf = torch.uint8, torch.int32, torch.bfloat16
+        e = lambda *s, dt=u8: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        sc = lambda r, c: e(*scale_shape(r, c))  # noqa: E731
+        self.xq, self.xs = e(T, H), sc(T, H)
+        self.xpq, self.xps = e(cap, H), sc(cap, H)
+        self.off, self.dst, self.src = e(E + 1, dt=i32), e(T * topk, dt=i32), e(cap, dt=i32)
+        self.wsb = mx_permute_workspace_size(T, topk, E)
+        self.ws = e(max(self.wsb, 4))
+        self.w1q, self.w1s = e(E, 2 * F, H), sc(E * 2 * F, H)
+        self.w1tq, self.w1ts = e(E, H, 2 * F), sc(E * H, 2 * F)
+        self.w2q, self.w2s = e(E, H, F), sc(E * H, F)
+        self.w2tq, self.w2ts = e(E, F, H), sc(E * F, H)
+        self.h = torch.zeros((cap, 2 * F), dtype=bf, device=device)
+        self.aq, self.as_ = e(cap, F), sc(cap, F)
+        self.atq, self.ats = e(F, cap), sc(F, cap)
+        self.y = e(cap, H, dt=bf)
+        self.out = e(T, H, dt=bf)
+        self.dyq, self.dys = e(cap, H), sc(cap, H)
+        self.dytq, self.dyts = e(H, cap), sc(H, cap)
+        self.da = torch.zeros((cap, F), dtype=bf, device=device)
+        self.dw2 = e(E, H, F, dt=bf)
+        self.dhq, self.dhs = e(cap, 2 * F), sc(cap, 2 * F)
+        self.dhtq, self.dhts = e(2 * F, cap), sc(2 * F, cap)
+        self.dxp = e(cap, H, dt=bf)
+        self.xtq, self.xts = e(H, cap), sc(H, cap)
+        self.dw1 = e(E, 2 * F, H, dt=bf)
+        self.dx = e(T, H, dt=bf)
+
+
+def run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream=None):
+    """Launch one named stage of the layer on ``stream`` (default: torch's current stream)."""
+    T, H, F, E, k, cap, bf = b.T, b.H, b.F, b.E, b.topk, b.cap, MX_OUT_BF16
+    if name == "quant_x":
+        mx_quantize(x, 1, T, H, None, T, b.xq, b.xs, None, None, stream)
+    elif name == "permute":
+        mx_permute(b.xq, b.xs, T, H, ids, k, E, cap, b.xpq, b.xps, b.off, b.dst, b.src, b.ws, b.wsb, stream)
+    elif name == "quant_w1":
+        mx_quantize(w1, E, 2 * F, H, None, 2 * F, b.w1q, b.w1s, b.w1tq, b.w1ts, stream)
+    elif name == "gemm1_fwd":
+        mx_grouped_gemm_fwd(b.xpq, b.xps, b.w1q, b.w1s, b.off, E, cap, 2 * F, H, b.h, bf, stream)
+    elif name == "swiglu":
+        mx_swiglu_quantize(b.h, cap, F, None, b.aq, b.as_, b.atq, b.ats, stream)
+    elif name == "quant_w2":
+        mx_quantize(w2, E, H, F, None, H, b.w2q, b.w2s, b.w2tq, b.w2ts, stream)
+    elif name == "gemm2_fwd":
+        mx_grouped_gemm_fwd(b.aq, b.as_, b.w2q, b.w2s, b.off, E, cap, H, F, b.y, bf, stream)
+    elif name == "combine":
+        mx_combine(b.y, cap, H, b.dst, weights, T, k, b.out, stream)
+    elif name == "combine_bwd":
+        mx_combine_bwd_quantize(dout, weights, b.dst, b.src, T, k, cap, H, None, b.dyq, b.dys, b.dytq, b.dyts,
+                                stream)
+    elif name == "gemm2_dgrad":
+        mx_grouped_gemm_dgrad(b.dyq, b.dys, b.w2tq, b.w2ts, b.off, E, cap, F, H, b.da, bf, stream)
+    elif name == "gemm2_wgrad":
+        mx_grouped_gemm_wgrad(b.dytq, b.dyts, b.atq, b.ats, b.off, E, cap, H, F, b.dw2, bf, stream)
+    elif name == "swiglu_bwd":
+        mx_swiglu_bwd_quantize(b.h, b.da, cap, F, None, b.dhq, b.dhs, b.dhtq, b.dhts, stream)
+    elif name == "gemm1_dgrad":
+        mx_grouped_gemm_dgrad(b.dhq, b.dhs, b.w1tq, b.w1ts, b.off, E, cap, H, 2 * F, b.dxp, bf, stream)
+    elif name == "quant_xt":
+        mx_quantize(x, 1, T, H, b.src, cap, None, None, b.xtq, b.xts, stream)
+    elif name == "gemm1_wgrad":
+        mx_grouped_gemm_wgrad(b.dhtq, b.dhts, b.xtq, b.xts, b.off, E, cap, 2 * F, H, b.dw1, bf, stream)
+    elif name == "unpermute_dx":
+        mx_combine(b.dxp, cap, H, b.dst, None, T, k, b.dx, stream)
+    else:
+        raise ValueError(name)
+
+
+def layer_step(b, x, w1, w2, ids, weights, dout, stream=None):
+    """One forward + backward pass of the SwiGLU expert FFN layer."""
+    for name in LAYER_STAGES:
+        run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream)
+
+
+def layer_work(T, H, F, E, topk):
+    """FLOPs of the six GEMMs (real routed rows only) and the algorithmic
+    bytes of every other stage (each tensor read or written once)."""
+    M = T * topk
+    cap = -(-(T * topk + 31 * E) // 32) * 32
+    mx = 1 + 1 / 32
+    g1 = 2.0 * M * 2 * F * H
+    g2 = 2.0 * M * H * F
+    return {
+        "gemm_flops": {"gemm1_fwd": g1, "gemm2_fwd": g2, "gemm2_dgrad": g2, "gemm2_wgrad": g2,
+                       "gemm1_dgrad": g1, "gemm1_wgrad": g1},
+        "bytes": {
+            "quant_x": T * H * (2 + mx),
+            "permute": H * mx * (T + cap) + 4 * (M * 2 + cap),
+            "quant_w1": E * 2 * F * H * (2 + 2 * mx),
+            "swiglu": cap * F * (4 + 2 * mx),                       # read g, u; write A row + col MX
+            "quant_w2": E * H * F * (2 + 2 * mx),
+            "combine": T * H * (2 * topk + 2) + M * 8,              # k rows in, one row out, ids + weights
+            "combine_bwd": T * H * 2 + cap * H * 2 * mx + M * 8 + cap * 4,
+            "swiglu_bwd": cap * F * 6 + cap * 2 * F * 2 * mx,       # read g, u, dA; write dH row + col MX
+            "quant_xt": M * H * 2 + cap * H * mx + 4 * cap,
+            "unpermute_dx": T * H * (2 * topk + 2) + M * 4,
         },
     }
