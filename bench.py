@@ -43,7 +43,8 @@ CALIB_BYTES = 1 << 30        # plain device copy used to scale the FETCH_SIZE / 
 def measured_traffic(stage):
     """HBM bytes per launch of ``stage`` as recorded in profiles/hbm_traffic.txt
     (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a copy of known size), or
-    None when no record exists or the kernel source changed since it was taken."""
+    None when no record exists or a kernel source changed since it was taken
+    (the record hashes its comma-separated source files, concatenated)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     for line in open(TRAFFIC_FILE):
@@ -52,8 +53,10 @@ def measured_traffic(stage):
         kv = dict(f.split("=", 1) for f in line.split())
         if kv.get("stage") != stage:
             continue
-        src = os.path.join(ROOT, kv["source"])
-        if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != kv["sha256"]:
+        srcs = [os.path.join(ROOT, f) for f in kv["source"].split(",")]
+        if not all(os.path.exists(f) for f in srcs):
+            return None
+        if hashlib.sha256(b"".join(open(f, "rb").read() for f in srcs)).hexdigest() != kv["sha256"]:
             return None
         return {"fetch_bytes": float(kv["fetch_bytes"]), "write_bytes": float(kv["write_bytes"]),
                 "bytes": float(kv["fetch_bytes"]) + float(kv["write_bytes"])}
@@ -125,6 +128,8 @@ def gpu_expert_path(args, c):
         else:
             gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
             stages[n] = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+        tr = measured_traffic(n)
+        stages[n]["traffic"] = None if tr is None else tr["bytes"]
     gemm_total = sum(work["gemm_flops"].values())
     value = gemm_total / (step_ms * 1e-3) / 1e12
     dom = max(work["gemm_flops"], key=lambda n: per[n])
@@ -236,6 +241,8 @@ def gpu_swiglu_layer(args):
         else:
             gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
             stages[n] = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+        tr = measured_traffic("layer." + n)
+        stages[n]["traffic"] = None if tr is None else tr["bytes"]
     flops = sum(work["gemm_flops"].values())
     tf = flops / (step_ms * 1e-3) / 1e12
     res = {"workload": "SwiGLU expert FFN layer fwd+bwd: T=32768 tokens, top-8 of E=64 experts (262144 routed "
