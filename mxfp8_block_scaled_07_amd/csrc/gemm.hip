@@ -185,13 +185,31 @@ __device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E,
   Coord c;
   const uint32_t L = (uint32_t)L64;
   if (!kWgrad) {
-    // rows of group e in tiles of 256; a group's tiles walked n-tile major
+    // rows of group e in tiles of 256; a group's tiles walked in bands of b
+    // m tiles, n-tile major inside a band.  The 32 tiles an XCD runs at once
+    // then form a b x 32/b block sharing b A and 32/b B row panels in its
+    // L2.  Over the group, A panels are fetched about n_tiles * b / 32 times
+    // and B panels once per band, so b minimizes mt_e * b + 32 * ceil(mt_e / b)
+    // (b = mt_e, one band, for small groups).
     const int e = find_group(sc, E, L64);
     const int32_t lo = uni(sc.bound[e]), hi = uni(sc.bound[e + 1]);
     const uint32_t mt_e = (uint32_t)(hi - lo + BM - 1) / BM;
     const uint32_t rem = L - (uint32_t)uni(sc.tiles_before[e]);
-    const uint32_t nt = rem / mt_e;
-    const uint32_t mt = rem - nt * mt_e;
+    uint32_t kBand = 1, best = ~0u;
+    for (uint32_t b = 1; b <= 8 && b <= mt_e; ++b) {
+      const uint32_t cost = mt_e * b + 32 * ((mt_e + b - 1) / b);
+      if (cost <= best) {
+        best = cost;
+        kBand = b;
+      }
+    }
+    const uint32_t per_band = kBand * (uint32_t)n_tiles;
+    const uint32_t band = rem / per_band;
+    const uint32_t first_m = band * kBand;
+    const uint32_t band_m = (mt_e - first_m) < kBand ? (mt_e - first_m) : kBand;
+    const uint32_t in_band = rem - band * per_band;
+    const uint32_t nt = in_band / band_m;
+    const uint32_t mt = first_m + (in_band - nt * band_m);
     c.e = e;
     c.row_a = lo + (int64_t)mt * BM;
     c.row_b = (int64_t)nt * BN;

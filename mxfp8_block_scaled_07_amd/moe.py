@@ -223,6 +223,15 @@ def layer_work(T, H, F, E, topk):
     return {
         "gemm_flops": {"gemm1_fwd": g1, "gemm2_fwd": g2, "gemm2_dgrad": g2, "gemm2_wgrad": g2,
                        "gemm1_dgrad": g1, "gemm1_wgrad": g1},
+        # MX operands (codes + scales) read once and the bf16 output written once
+        "gemm_operand_bytes": {
+            "gemm1_fwd": (M * H + E * 2 * F * H) * mx + M * 2 * F * 2,
+            "gemm2_fwd": (M * F + E * H * F) * mx + M * H * 2,
+            "gemm2_dgrad": (M * H + E * F * H) * mx + M * F * 2,
+            "gemm2_wgrad": (H * M + F * M) * mx + E * H * F * 2,
+            "gemm1_dgrad": (M * 2 * F + E * H * 2 * F) * mx + M * H * 2,
+            "gemm1_wgrad": (2 * F * M + H * M) * mx + E * 2 * F * H * 2,
+        },
         "bytes": {
             "quant_x": T * H * (2 + mx),
             "permute": H * mx * (T + cap) + 4 * (M * 2 + cap),
