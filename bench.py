@@ -194,38 +194,20 @@ def gpu_quantize_bandwidth(args):
 
 def gpu_swiglu_layer(args):
     """The full SwiGLU expert FFN layer of the 64-expert top-8 workload (T=32768
-    tokens, hidden 7168, expert ffn 2048), forward plus backward, on seeded
-    synthetic inputs generated on the GPU: router logits N(0,1) -> top-8 and
-    softmax weights over the 8, X and dOut bf16 N(0,1), W1 [64, 4096, 7168] and
-    W2 [64, 7168, 2048] bf16 0.02*N(0,1).  Every stage is timed like the
-    headline step; the glue kernels (SwiGLU, combine and their backwards) are
-    reported against HBM bandwidth."""
+    tokens, hidden 7168, expert ffn 2048), forward plus backward, on the seeded
+    synthetic inputs of ``workloads.layer_inputs`` (drawn on the GPU).  Every
+    stage is timed like the headline step; the glue kernels (SwiGLU, combine
+    and their backwards) are reported against HBM bandwidth."""
     import torch
 
     from mxfp8_block_scaled_07_amd import moe
 
-    T, H, F, E, k = 32768, 7168, 2048, 64, 8
+    import workloads
+    inp = workloads.layer_inputs("cuda:0")
+    T, H, F, E, k = inp["T"], inp["H"], inp["F"], inp["E"], inp["topk"]
     dev = "cuda:0"
-    g = torch.Generator(device=dev)
-    g.manual_seed(5)
-
-    def normal_bf16(shape, std):
-        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
-        flat = out.view(-1)
-        ch = 1 << 26               # chunked: keeps the fp32 temporary small
-        for i in range(0, flat.numel(), ch):
-            n = min(ch, flat.numel() - i)
-            flat[i:i + n] = (torch.randn(n, generator=g, device=dev) * std).to(torch.bfloat16)
-        return out
-
-    logits = torch.randn((T, E), generator=g, device=dev)
-    top = torch.topk(logits, k, dim=1)
-    ids = top.indices.to(torch.int32).contiguous()
-    weights = torch.softmax(top.values, dim=1).float().contiguous()
-    x = normal_bf16((T, H), 1.0)
-    dout = normal_bf16((T, H), 1.0)
-    w1 = normal_bf16((E, 2 * F, H), 0.02)
-    w2 = normal_bf16((E, H, F), 0.02)
+    ids, weights, x, dout, w1, w2 = inp["ids"], inp["weights"], inp["x"], inp["dout"], inp["w1"], inp["w2"]
+    del inp
     b = moe.LayerBuffers(T, H, F, E, k, device=dev)
     torch.cuda.synchronize()
     steps = max(3, args.steps // 4)

@@ -21,6 +21,8 @@ inputs):
                   forced empty, 0.1% outliers x1000 in X, W and dY
 4. quantize bandwidth  [16*8192, 5120], 1% all-zero 32x32 tiles, 1%
                   subnormal 32x32 tiles, 0.1% outliers x1000
+5. SwiGLU expert FFN layer  T=32768 tokens, top-8 of E=64, hidden 7168,
+                  expert ffn 2048 (``layer_inputs``: drawn on the GPU)
 """
 
 import numpy as np
@@ -169,3 +171,39 @@ def quant_tensor(cfg, rows, cols, zero_p=0.01, sub_p=0.01, outlier_p=0.001, chun
     sign = (tg.integers(0, 2, nsub).astype(np.uint16) << 15)
     xv[st] = mant | sign
     return x
+
+
+LAYER5 = {"T": 32768, "H": 7168, "F": 2048, "E": 64, "topk": 8}
+
+
+def layer_inputs(device="cuda:0", seed=5, T=32768, H=7168, F=2048, E=64, topk=8):
+    """Workload-5 inputs drawn on the GPU with a seeded torch generator (the
+    weights alone are 5.6 G elements): router logits N(0,1) [T, E] -> top-k
+    ids (int32) and softmax weights over the k chosen logits (fp32); X and
+    dOut bf16 N(0,1) [T, H]; W1 [E, 2F, H] (gate rows then up rows) and W2
+    [E, H, F] bf16 0.02 * N(0,1).  Samples are fp32, scaled, then rounded to
+    bf16 (RNE, torch's conversion)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def normal_bf16_gpu(shape, std):
+        out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+        flat = out.view(-1)
+        ch = 1 << 26               # chunked: keeps the fp32 temporary small
+        for i in range(0, flat.numel(), ch):
+            n = min(ch, flat.numel() - i)
+            flat[i:i + n] = (torch.randn(n, generator=g, device=device) * std).to(torch.bfloat16)
+        return out
+
+    logits = torch.randn((T, E), generator=g, device=device)
+    top = torch.topk(logits, topk, dim=1)
+    return {
+        "T": T, "H": H, "F": F, "E": E, "topk": topk,
+        "ids": top.indices.to(torch.int32).contiguous(),
+        "weights": torch.softmax(top.values, dim=1).float().contiguous(),
+        "x": normal_bf16_gpu((T, H), 1.0),
+        "dout": normal_bf16_gpu((T, H), 1.0),
+        "w1": normal_bf16_gpu((E, 2 * F, H), 0.02),
+        "w2": normal_bf16_gpu((E, H, F), 0.02),
+    }
