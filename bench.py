@@ -206,12 +206,12 @@ def gpu_swiglu_layer(args):
     inp = workloads.layer_inputs("cuda:0")
     T, H, F, E, k = inp["T"], inp["H"], inp["F"], inp["E"], inp["topk"]
     dev = "cuda:0"
-    ids, weights, x, dout, w1, w2 = inp["ids"], inp["weights"], inp["x"], inp["dout"], inp["w1"], inp["w2"]
+    logits, x, dout, w1, w2 = inp["logits"], inp["x"], inp["dout"], inp["w1"], inp["w2"]
     del inp
     b = moe.LayerBuffers(T, H, F, E, k, device=dev)
     torch.cuda.synchronize()
     steps = max(3, args.steps // 4)
-    step_ms, per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, ids, weights, dout),
+    step_ms, per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, logits, dout),
                                   moe.LAYER_STAGES, steps, 2)
     work = moe.layer_work(T, H, F, E, k)
     stages = {}
@@ -227,12 +227,12 @@ def gpu_swiglu_layer(args):
         stages[n]["traffic"] = None if tr is None else tr["bytes"]
     flops = sum(work["gemm_flops"].values())
     tf = flops / (step_ms * 1e-3) / 1e12
-    res = {"workload": "SwiGLU expert FFN layer fwd+bwd: T=32768 tokens, top-8 of E=64 experts (262144 routed "
-                       "rows), hidden 7168, expert ffn 2048, bf16 N(0,1) activations, 0.02*N(0,1) weights, "
-                       "MXFP8 GEMM operands, bf16 GEMM outputs",
+    res = {"workload": "SwiGLU expert FFN layer fwd+bwd from router logits: T=32768 tokens, top-8 of E=64 experts "
+                       "(262144 routed rows), hidden 7168, expert ffn 2048, bf16 N(0,1) activations, 0.02*N(0,1) "
+                       "weights, MXFP8 GEMM operands, bf16 GEMM outputs",
            "steps": steps, "ms_per_step": round(step_ms, 3), "gemm_tflop_per_step": round(flops / 1e12, 3),
            "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4), "stages": stages}
-    del b, x, dout, w1, w2
+    del b, x, dout, w1, w2, logits
     torch.cuda.empty_cache()
     return res
 

@@ -233,6 +233,37 @@ int mx_combine_bwd_quantize(const uint16_t* dout, const float* weights, const in
                             const int32_t* src_row, int64_t tokens, int32_t topk, int64_t rows, int64_t H, uint16_t* dy,
                             uint8_t* row_q, uint8_t* row_s, uint8_t* col_q, uint8_t* col_s, mx_stream_t stream);
 
+/*
+ * Router: top-k expert choice with softmax weights, in front of mx_permute.
+ * The pages give no router formula (digest "Overview": an MXFP8 MoE layer);
+ * the reading: a token's experts are its k largest logits, equal logits to
+ * the lower expert id, in decreasing order; the weights are the softmax of
+ * the k chosen logits (fp32, renormalised over the chosen experts).
+ *   logits      fp32 [tokens, num_experts]
+ *   expert_ids  int32 [tokens, topk] (the layout mx_permute takes)
+ *   weights     fp32 [tokens, topk] (the layout mx_combine takes)
+ * Requires 1 <= topk <= num_experts; num_experts <= 1024 and topk <= 64
+ * (else MX_EUNSUPPORTED).  NaN logits are outside the contract.
+ */
+int mx_route_topk(const float* logits, int64_t tokens, int32_t num_experts, int32_t topk, int32_t* expert_ids,
+                  float* weights, mx_stream_t stream);
+
+/*
+ * Router backward through the weighted combine: with out[t] = sum_j w[t,j]
+ * y[dst_row[t topk + j]],
+ *   dw[t,j]          = <dout[t], y[dst_row[t topk + j]]>  (fp32 [tokens, topk])
+ *   dlogits[t, e]    = w[t,j] (dw[t,j] - sum_i w[t,i] dw[t,i]) for e = expert_ids[t,j],
+ *                      0 for experts not chosen  (fp32 [tokens, num_experts])
+ *   dout bf16 [tokens, H]; y bf16 [y_rows, H] (the combine's input rows);
+ *   dst_row int32 [tokens * topk]; weights fp32 [tokens, topk].
+ * Either output may be NULL (not both); expert_ids is needed with dlogits.
+ * fp32 accumulation.  Requires H % 32 == 0, topk <= 64; dout and y 16-byte
+ * aligned.  A dst_row entry outside [0, y_rows) contributes nothing.
+ */
+int mx_router_bwd(const uint16_t* dout, const uint16_t* y, int64_t y_rows, int64_t H, const int32_t* dst_row,
+                  const int32_t* expert_ids, const float* weights, int64_t tokens, int32_t num_experts, int32_t topk,
+                  float* dw, float* dlogits, mx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,8 @@ _SIGNATURES = {
     "mx_combine": (ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _i64, _i32, _vp, _vp]),
     "mx_combine_bwd_quantize": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                                _vp]),
+    "mx_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "mx_router_bwd": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
 }
 
 
@@ -131,6 +133,17 @@ def mx_combine_bwd_quantize(dout, weights, dst_row, src_row, tokens, topk, rows,
     _check(lib().mx_combine_bwd_quantize(_p(dout), _p(weights), _p(dst_row), _p(src_row), tokens, topk, rows, H,
                                          _p(dy), _p(row_q), _p(row_s), _p(col_q), _p(col_s), _s(stream)),
            "mx_combine_bwd_quantize")
+
+
+def mx_route_topk(logits, tokens, num_experts, topk, expert_ids, weights, stream=None):
+    _check(lib().mx_route_topk(_p(logits), tokens, num_experts, topk, _p(expert_ids), _p(weights), _s(stream)),
+           "mx_route_topk")
+
+
+def mx_router_bwd(dout, y, y_rows, H, dst_row, expert_ids, weights, tokens, num_experts, topk, dw, dlogits,
+                  stream=None):
+    _check(lib().mx_router_bwd(_p(dout), _p(y), y_rows, H, _p(dst_row), _p(expert_ids), _p(weights), tokens,
+                               num_experts, topk, _p(dw), _p(dlogits), _s(stream)), "mx_router_bwd")
 
 
 # --- allocating helpers ----------------------------------------------------
@@ -242,3 +255,26 @@ def combine_bwd_quantize(dout, weights, dst_row, src_row, topk, rows, rowwise=Tr
         mx_combine_bwd_quantize(dout if tokens else None, weights if tokens else None, dst_row if tokens else None,
                                 src_row, tokens, topk, rows, H, dy, rq, rs, cq, cs, stream)
     return dy, rq, rs, cq, cs
+
+
+def route_topk(logits, topk, stream=None):
+    """logits: fp32 [tokens, E].  Returns (expert_ids int32 [tokens, topk], weights fp32 [tokens, topk])."""
+    import torch
+    T, E = logits.shape
+    ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    if T:
+        mx_route_topk(logits, T, E, topk, ids, w, stream)
+    return ids, w
+
+
+def router_bwd(dout, y, dst_row, expert_ids, weights, num_experts, stream=None):
+    """Returns (dw fp32 [tokens, topk], dlogits fp32 [tokens, num_experts])."""
+    import torch
+    T, topk = weights.shape
+    dw = torch.empty((T, topk), dtype=torch.float32, device=dout.device)
+    dl = torch.empty((T, num_experts), dtype=torch.float32, device=dout.device)
+    if T:
+        mx_router_bwd(dout, y, y.shape[0], y.shape[1], dst_row, expert_ids, weights, T, num_experts, topk, dw, dl,
+                      stream)
+    return dw, dl

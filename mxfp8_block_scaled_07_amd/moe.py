@@ -23,7 +23,7 @@ import torch
 
 from . import (MX_OUT_BF16, MX_OUT_F32, mx_combine, mx_combine_bwd_quantize, mx_grouped_gemm_dgrad,
                mx_grouped_gemm_fwd, mx_grouped_gemm_wgrad, mx_permute, mx_permute_workspace_size, mx_quantize,
-               mx_swiglu_bwd_quantize, mx_swiglu_quantize, scale_shape)
+               mx_route_topk, mx_router_bwd, mx_swiglu_bwd_quantize, mx_swiglu_quantize, scale_shape)
 
 STAGES = ("quant_x", "permute", "quant_w", "gemm_fwd", "quant_dy", "gemm_dgrad", "quant_xt", "gemm_wgrad")
 
@@ -118,14 +118,14 @@ def algorithmic_work(T, K, N, E, topk, m_real=None):
 
 
 # ---------------------------------------------------------------------------
-# The SwiGLU expert FFN layer: gate/up GEMM -> SwiGLU -> down GEMM ->
-# weighted combine, forward and backward, every operand of every GEMM in
-# MXFP8.  W1 [E, 2F, H] holds the gate rows [0, F) and the up rows [F, 2F)
+# The SwiGLU expert FFN layer: router -> permute -> gate/up GEMM -> SwiGLU ->
+# down GEMM -> weighted combine, forward and backward (down to the router
+# logits), every operand of every GEMM in MXFP8.  W1 [E, 2F, H] holds the gate rows [0, F) and the up rows [F, 2F)
 # of each expert; W2 [E, H, F].
 # ---------------------------------------------------------------------------
-LAYER_STAGES = ("quant_x", "permute", "quant_w1", "gemm1_fwd", "swiglu", "quant_w2", "gemm2_fwd", "combine",
-                "combine_bwd", "gemm2_dgrad", "gemm2_wgrad", "swiglu_bwd", "gemm1_dgrad", "quant_xt",
-                "gemm1_wgrad", "unpermute_dx")
+LAYER_STAGES = ("router", "quant_x", "permute", "quant_w1", "gemm1_fwd", "swiglu", "quant_w2", "gemm2_fwd",
+                "combine", "combine_bwd", "router_bwd", "gemm2_dgrad", "gemm2_wgrad", "swiglu_bwd", "gemm1_dgrad",
+                "quant_xt", "gemm1_wgrad", "unpermute_dx")
 
 
 class LayerBuffers:
@@ -142,9 +142,11 @@ class LayerBuffers:
         sc = lambda r, c: e(*scale_shape(r, c))  # noqa: E731
         self.xq, self.xs = e(T, H), sc(T, H)
         self.xpq, self.xps = e(cap, H), sc(cap, H)
+        self.ids, self.weights = e(T, topk, dt=i32), e(T, topk, dt=torch.float32)
         self.off, self.dst, self.src = e(E + 1, dt=i32), e(T * topk, dt=i32), e(cap, dt=i32)
         self.wsb = mx_permute_workspace_size(T, topk, E)
         self.ws = e(max(self.wsb, 4))
+        self.dweights, self.dlogits = e(T, topk, dt=torch.float32), e(T, E, dt=torch.float32)
         self.w1q, self.w1s = e(E, 2 * F, H), sc(E * 2 * F, H)
         self.w1tq, self.w1ts = e(E, H, 2 * F), sc(E * H, 2 * F)
         self.w2q, self.w2s = e(E, H, F), sc(E * H, F)
@@ -166,10 +168,13 @@ class LayerBuffers:
         self.dx = e(T, H, dt=bf)
 
 
-def run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream=None):
+def run_layer_stage(name, b, x, w1, w2, logits, dout, stream=None):
     """Launch one named stage of the layer on ``stream`` (default: torch's current stream)."""
     T, H, F, E, k, cap, bf = b.T, b.H, b.F, b.E, b.topk, b.cap, MX_OUT_BF16
-    if name == "quant_x":
+    ids, weights = b.ids, b.weights
+    if name == "router":
+        mx_route_topk(logits, T, E, k, b.ids, b.weights, stream)
+    elif name == "quant_x":
         mx_quantize(x, 1, T, H, None, T, b.xq, b.xs, None, None, stream)
     elif name == "permute":
         mx_permute(b.xq, b.xs, T, H, ids, k, E, cap, b.xpq, b.xps, b.off, b.dst, b.src, b.ws, b.wsb, stream)
@@ -188,6 +193,8 @@ def run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream=None):
     elif name == "combine_bwd":
         mx_combine_bwd_quantize(dout, weights, b.dst, b.src, T, k, cap, H, None, b.dyq, b.dys, b.dytq, b.dyts,
                                 stream)
+    elif name == "router_bwd":
+        mx_router_bwd(dout, b.y, cap, H, b.dst, b.ids, b.weights, T, E, k, b.dweights, b.dlogits, stream)
     elif name == "gemm2_dgrad":
         mx_grouped_gemm_dgrad(b.dyq, b.dys, b.w2tq, b.w2ts, b.off, E, cap, F, H, b.da, bf, stream)
     elif name == "gemm2_wgrad":
@@ -206,10 +213,10 @@ def run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream=None):
         raise ValueError(name)
 
 
-def layer_step(b, x, w1, w2, ids, weights, dout, stream=None):
+def layer_step(b, x, w1, w2, logits, dout, stream=None):
     """One forward + backward pass of the SwiGLU expert FFN layer."""
     for name in LAYER_STAGES:
-        run_layer_stage(name, b, x, w1, w2, ids, weights, dout, stream)
+        run_layer_stage(name, b, x, w1, w2, logits, dout, stream)
 
 
 def layer_work(T, H, F, E, topk):
@@ -233,6 +240,8 @@ def layer_work(T, H, F, E, topk):
             "gemm1_wgrad": (2 * F * M + H * M) * mx + E * 2 * F * H * 2,
         },
         "bytes": {
+            "router": T * E * 4 + M * 8,                            # logits in, ids + weights out
+            "router_bwd": T * H * (2 * topk + 2) + M * 16 + T * E * 4,   # dOut and k rows of Y in, dw + dlogits out
             "quant_x": T * H * (2 + mx),
             "permute": H * mx * (T + cap) + 4 * (M * 2 + cap),
             "quant_w1": E * 2 * F * H * (2 + 2 * mx),

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"mx_quantize", "mx_dequantize", "mx_permute", "mx_permute_workspace_size",
                           "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
                           "mx_status_string", "mx_swiglu_quantize", "mx_swiglu_bwd_quantize", "mx_combine",
-                          "mx_combine_bwd_quantize"}
+                          "mx_combine_bwd_quantize", "mx_route_topk", "mx_router_bwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -129,6 +129,21 @@ def test_combine_validation(lib):
     assert b(P, P, P, P, 8, 2, 40, 64, None, None, None, P, P, None) == mxa.MX_EINVAL        # colwise rows % 32
     assert b(P, P, P, P, 8, 2, 64, 64, None, None, None, None, None, None) == mxa.MX_EINVAL  # no output
     assert b(P, P, P, P, 8, 2, 0, 64, P, None, None, None, None, None) == mxa.MX_OK
+
+
+def test_router_validation(lib):
+    r = lib.mx_route_topk
+    assert r(None, 8, 16, 2, P, P, None) == mxa.MX_EINVAL                                 # logits null
+    assert r(P, 8, 16, 0, P, P, None) == mxa.MX_EINVAL                                    # topk 0
+    assert r(P, 8, 4, 5, P, P, None) == mxa.MX_EINVAL                                     # topk > E
+    assert r(P, 8, 2048, 2, P, P, None) == mxa.MX_EUNSUPPORTED                            # E > 1024
+    assert r(P, 0, 16, 2, P, P, None) == mxa.MX_OK                                        # no tokens
+    b = lib.mx_router_bwd
+    assert b(P, P, 64, 64, P, P, P, 8, 16, 2, None, None, None) == mxa.MX_EINVAL         # no output
+    assert b(P, P, 64, 48, P, P, P, 8, 16, 2, P, None, None) == mxa.MX_EINVAL            # H % 32
+    assert b(P, P, 64, 64, P, None, P, 8, 16, 2, None, P, None) == mxa.MX_EINVAL         # dlogits needs ids
+    assert b(Q, P, 64, 64, P, P, P, 8, 16, 2, P, None, None) == mxa.MX_EINVAL            # alignment
+    assert b(P, P, 64, 64, P, P, P, 0, 16, 2, P, P, None) == mxa.MX_OK
 
 
 def test_python_binding_raises(lib):

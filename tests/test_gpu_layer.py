@@ -20,7 +20,7 @@ import workloads
 from mxfp8_block_scaled_07_amd import moe
 from oracle import glue
 from oracle import mxfp8 as mx
-from oracle import routing, tolerance
+from oracle import router, routing, tolerance
 
 from gpu_util import host
 
@@ -51,9 +51,12 @@ def layer():
     inp = workloads.layer_inputs("cuda:0")
     T, H, F, E, k = inp["T"], inp["H"], inp["F"], inp["E"], inp["topk"]
     b = moe.LayerBuffers(T, H, F, E, k)
-    moe.layer_step(b, inp["x"], inp["w1"], inp["w2"], inp["ids"], inp["weights"], inp["dout"])
+    moe.layer_step(b, inp["x"], inp["w1"], inp["w2"], inp["logits"], inp["dout"])
     torch.cuda.synchronize()
-    ids = host(inp["ids"])
+    ids, w = router.route_topk(host(inp["logits"]), k)
+    assert np.array_equal(host(b.ids), ids)
+    assert np.all(np.abs(host(b.weights) - w) <= 2.0 ** -20 * w)
+    inp["weights"] = b.weights
     _, off, dst, src = routing.route(ids, E, b.cap)
     return inp, b, off, dst, src
 
@@ -174,6 +177,14 @@ def test_combine_bwd_and_down_backward(layer):
     dyr[local] = sub
     oq, os_ = mx.quantize_rowwise(dyr)
     assert np.array_equal(rows(b.dyq, r), oq) and np.array_equal(srow_sel(b.dys, H, r), os_)
+    # router backward: sampled tokens, from the kernel's own Y rows and weights
+    ts = np.sort(g.choice(T, 32, replace=False))
+    pairs = (ts[:, None] * k + np.arange(k)).ravel()
+    edw, sdw, edl, sdl = glue_router_bwd(inp, b, ts, pairs, dst, k)
+    rel = (H / 64 + 8) * 2.0 ** -24
+    gdw, gdl = host(b.dweights)[ts], host(b.dlogits)[ts]
+    assert np.all(np.abs(gdw - edw) <= rel * sdw + 2.0 ** -126), "router dw"
+    assert np.all(np.abs(gdl - edl) <= rel * sdl + 2.0 ** -126), "router dlogits"
     # dA = dY W2 (dgrad), from the kernel's own dY rows and W2^T columnwise bytes
     m, f, grp = row_gemm_samples(g, b, off, src, F)
     got = host(b.da[ix(m), ix(f)])
@@ -181,6 +192,13 @@ def test_combine_bwd_and_down_backward(layer):
           srow_sel(b.w2ts, H, grp * F + f))
     # dW2[e] = dY_e^T A_e (wgrad over the group's rows)
     wgrad_samples(g, "gemm2_wgrad", b.dw2, off, b.dytq, b.dyts, b.atq, b.ats, H, F, b.cap)
+
+
+def glue_router_bwd(inp, b, ts, pairs, dst, k):
+    """The oracle's router backward for tokens ts, on the kernel's Y rows and weights."""
+    ysub = rows(b.y, dst[pairs])
+    return router.router_bwd(rows(inp["dout"], ts), ysub, np.arange(pairs.size), host(b.ids)[ts],
+                             host(b.weights)[ts], inp["E"])
 
 
 def wgrad_samples(g, name, dw, off, aq_t, as_t, bq_t, bs_t, N, K, cap, nsamp=96):

@@ -178,11 +178,10 @@ LAYER5 = {"T": 32768, "H": 7168, "F": 2048, "E": 64, "topk": 8}
 
 def layer_inputs(device="cuda:0", seed=5, T=32768, H=7168, F=2048, E=64, topk=8):
     """Workload-5 inputs drawn on the GPU with a seeded torch generator (the
-    weights alone are 5.6 G elements): router logits N(0,1) [T, E] -> top-k
-    ids (int32) and softmax weights over the k chosen logits (fp32); X and
-    dOut bf16 N(0,1) [T, H]; W1 [E, 2F, H] (gate rows then up rows) and W2
-    [E, H, F] bf16 0.02 * N(0,1).  Samples are fp32, scaled, then rounded to
-    bf16 (RNE, torch's conversion)."""
+    weights alone are 5.6 G elements): router logits fp32 N(0,1) [T, E]; X
+    and dOut bf16 N(0,1) [T, H]; W1 [E, 2F, H] (gate rows then up rows) and
+    W2 [E, H, F] bf16 0.02 * N(0,1).  Samples are fp32, scaled, then rounded
+    to bf16 (RNE, torch's conversion)."""
     import torch
     g = torch.Generator(device=device)
     g.manual_seed(seed)
@@ -197,11 +196,9 @@ def layer_inputs(device="cuda:0", seed=5, T=32768, H=7168, F=2048, E=64, topk=8)
         return out
 
     logits = torch.randn((T, E), generator=g, device=device)
-    top = torch.topk(logits, topk, dim=1)
     return {
         "T": T, "H": H, "F": F, "E": E, "topk": topk,
-        "ids": top.indices.to(torch.int32).contiguous(),
-        "weights": torch.softmax(top.values, dim=1).float().contiguous(),
+        "logits": logits,
         "x": normal_bf16_gpu((T, H), 1.0),
         "dout": normal_bf16_gpu((T, H), 1.0),
         "w1": normal_bf16_gpu((E, 2 * F, H), 0.02),
