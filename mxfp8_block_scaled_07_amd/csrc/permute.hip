@@ -7,7 +7,8 @@
 // each token's E4M3 codes and E8M0 scales together, untouched.
 //
 // Deterministic, stable ranks without ordering atomics:
-//   1. k_route_hist   per tile of kTile flat pairs, an expert histogram
+//   1. k_route_hist   per routing tile (512 flat pairs; 4096 above 1024
+//                     experts), an expert histogram
 //   2. k_route_scan   counts, padded exclusive scan -> group_offsets, and the
 //                     first row of every (tile, expert)
 //   3. k_route_rank   one wave per tile walks its pairs in flat order; a pair's
@@ -20,15 +21,18 @@
 namespace mx {
 namespace {
 
-constexpr int kTile = 4096;  // flat (token, slot) pairs per routing tile
+// Flat (token, slot) pairs per routing tile: small tiles keep many waves
+// ranking at once; with many experts the per-tile tables (hist, base: tiles x
+// experts) would grow, so large expert counts use larger tiles.
+inline int32_t route_tile(int32_t num_experts) { return num_experts <= 1024 ? 512 : 4096; }
 
 __global__ void __launch_bounds__(256) k_route_hist(const int32_t* __restrict__ ids, int64_t n, int32_t E,
-                                                    int32_t* __restrict__ hist) {
+                                                    int32_t tile, int32_t* __restrict__ hist) {
   extern __shared__ int32_t lh[];
   for (int e = threadIdx.x; e < E; e += blockDim.x) lh[e] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kTile;
-  for (int i = threadIdx.x; i < kTile; i += blockDim.x) {
+  const int64_t base = (int64_t)blockIdx.x * tile;
+  for (int i = threadIdx.x; i < tile; i += blockDim.x) {
     const int64_t f = base + i;
     if (f < n) {
       const int32_t e = ids[f];
@@ -39,17 +43,33 @@ __global__ void __launch_bounds__(256) k_route_hist(const int32_t* __restrict__ 
   for (int e = threadIdx.x; e < E; e += blockDim.x) hist[(int64_t)blockIdx.x * E + e] = lh[e];
 }
 
-// One block; thread e owns expert e (loops when E > blockDim).
+// One block of 1024 threads = 32 experts x 32 tile groups at a time: each
+// thread sums (then prefix-sums) its group's tiles for its expert.  Pass 1
+// gives every expert's count; the padded exclusive scan over experts gives
+// group_offsets; pass 2 writes, for every (tile, expert), the first row of
+// that tile's pairs of that expert.
 __global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__ hist, int32_t ntiles, int32_t E,
                                                      int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
-  extern __shared__ int32_t padded[];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+  extern __shared__ int32_t padded[];       // E entries
+  __shared__ int32_t part[32][33];          // [expert in chunk][tile group]
+  const int le = threadIdx.x & 31, grp = threadIdx.x >> 5;
+  const int32_t per = (ntiles + 31) / 32;
+  const int32_t t0 = grp * per, t1 = t0 + per < ntiles ? t0 + per : ntiles;
+  for (int32_t e0 = 0; e0 < E; e0 += 32) {
+    const int32_t e = e0 + le;
     int32_t c = 0;
-    for (int t = 0; t < ntiles; ++t) c += hist[(int64_t)t * E + e];
-    padded[e] = (c + 31) & ~31;
+    if (e < E)
+      for (int32_t t = t0; t < t1; ++t) c += hist[(int64_t)t * E + e];
+    part[le][grp] = c;
+    __syncthreads();
+    if (grp == 0 && e < E) {
+      int32_t tot = 0;
+      for (int g = 0; g < 32; ++g) tot += part[le][g];
+      padded[e] = (tot + 31) & ~31;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {  // E is small (experts): a serial scan is plenty
+  if (threadIdx.x == 0) {  // padded exclusive scan over experts
     int32_t acc = 0;
     for (int e = 0; e < E; ++e) {
       const int32_t p = padded[e];
@@ -60,12 +80,22 @@ __global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__
     offsets[E] = acc;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int32_t acc = padded[e];
-    for (int t = 0; t < ntiles; ++t) {
-      base[(int64_t)t * E + e] = acc;
-      acc += hist[(int64_t)t * E + e];
+  for (int32_t e0 = 0; e0 < E; e0 += 32) {
+    const int32_t e = e0 + le;
+    int32_t c = 0;
+    if (e < E)
+      for (int32_t t = t0; t < t1; ++t) c += hist[(int64_t)t * E + e];
+    part[le][grp] = c;
+    __syncthreads();
+    if (e < E) {
+      int32_t acc = padded[e];
+      for (int g = 0; g < grp; ++g) acc += part[le][g];
+      for (int32_t t = t0; t < t1; ++t) {
+        base[(int64_t)t * E + e] = acc;
+        acc += hist[(int64_t)t * E + e];
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -75,8 +105,9 @@ __global__ void __launch_bounds__(256) k_fill_i32(int32_t* __restrict__ p, int64
 
 // One wave (64 lanes) per tile.
 __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ ids, int64_t n, int32_t topk, int32_t E,
-                                                   const int32_t* __restrict__ base, int32_t* __restrict__ dst_row,
-                                                   int32_t* __restrict__ src_row, int64_t capacity) {
+                                                   int32_t tile, const int32_t* __restrict__ base,
+                                                   int32_t* __restrict__ dst_row, int32_t* __restrict__ src_row,
+                                                   int64_t capacity) {
   extern __shared__ int32_t next_row[];
   const int lane = threadIdx.x;
   for (int e = lane; e < E; e += 64) next_row[e] = base[(int64_t)blockIdx.x * E + e];
@@ -84,8 +115,8 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t t0 = (int64_t)blockIdx.x * kTile;
-  for (int c = 0; c < kTile; c += 64) {
+  const int64_t t0 = (int64_t)blockIdx.x * tile;
+  for (int c = 0; c < tile; c += 64) {
     const int64_t f = t0 + c + lane;
     int32_t e = -1;
     if (f < n) e = ids[f];
@@ -139,11 +170,14 @@ __global__ void __launch_bounds__(256) k_permute_rows(const uint8_t* __restrict_
 
 using namespace mx;
 
-static int64_t route_tiles(int64_t n) { return (n + kTile - 1) / kTile; }
+static int64_t route_tiles(int64_t n, int32_t num_experts) {
+  const int32_t t = route_tile(num_experts);
+  return (n + t - 1) / t;
+}
 
 extern "C" size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_experts) {
   if (tokens < 0 || topk < 1 || num_experts < 1) return 0;
-  const int64_t nt = route_tiles(tokens * topk);
+  const int64_t nt = route_tiles(tokens * topk, num_experts);
   return (size_t)(2 * (nt > 0 ? nt : 1) * num_experts) * sizeof(int32_t);
 }
 
@@ -160,26 +194,26 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
   if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int64_t nt = route_tiles(n) > 0 ? route_tiles(n) : 1;
+  const int32_t tile = route_tile(num_experts);
+  const int64_t nt = route_tiles(n, num_experts) > 0 ? route_tiles(n, num_experts) : 1;
   if (nt > 0x7FFFFFFF) return MX_EINVAL;
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* base = hist + nt * num_experts;
   const size_t lds = (size_t)num_experts * sizeof(int32_t);
   if (lds > 64 * 1024) return MX_EINVAL;
   if (n > 0) {
-    hipLaunchKernelGGL(k_route_hist, dim3((unsigned)route_tiles(n)), dim3(256), lds, st, expert_ids, n, num_experts,
-                       hist);
+    hipLaunchKernelGGL(k_route_hist, dim3((unsigned)nt), dim3(256), lds, st, expert_ids, n, num_experts, tile, hist);
   } else {
     hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, hist, (int64_t)num_experts, 0);
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), lds, st, hist, (int32_t)(n > 0 ? route_tiles(n) : 1),
-                     num_experts, base, group_offsets);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), lds, st, hist, (int32_t)nt, num_experts, base,
+                     group_offsets);
   const int64_t fill_blocks = (capacity_rows + 255) / 256 < 65536 ? (capacity_rows + 255) / 256 : 65536;
   if (capacity_rows > 0)
     hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)fill_blocks), dim3(256), 0, st, src_row, capacity_rows, -1);
   if (n > 0)
-    hipLaunchKernelGGL(k_route_rank, dim3((unsigned)route_tiles(n)), dim3(64), lds, st, expert_ids, n, topk,
-                       num_experts, base, dst_row, src_row, capacity_rows);
+    hipLaunchKernelGGL(k_route_rank, dim3((unsigned)nt), dim3(64), lds, st, expert_ids, n, topk, num_experts, tile,
+                       base, dst_row, src_row, capacity_rows);
   if (copy && capacity_rows > 0)
     hipLaunchKernelGGL(k_permute_rows, dim3((unsigned)((capacity_rows + 3) / 4)), dim3(256), 0, st, q, s, tokens,
                        cols, src_row, capacity_rows, q_out, s_out);
