@@ -18,8 +18,9 @@ throughput against the MI355X peak (MXFP8 dense 5.0 PFLOP/s, HBM 8 TB/s).
 the fused rowwise+columnwise quantize and both dequantizes of a
 [16*8192, 5120] bf16 tensor.  ``swiglu_layer`` times the full SwiGLU expert
 FFN layer (64 experts, top-8, 32768 tokens, hidden 7168, ffn 2048) forward
-plus backward, stage by stage, including the SwiGLU and combine glue.  ``cpu_baseline`` times the oracle on a bounded
-sample (three median-sized experts' share of the step).
+plus backward, stage by stage, including the router, SwiGLU and combine
+glue.  ``cpu_baseline`` times the oracle on a bounded sample (three
+median-sized experts' share of the step).
 """
 
 import argparse

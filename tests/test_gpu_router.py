@@ -44,7 +44,7 @@ def test_route_topk(T, E, k):
     check_close(host(w), ow, ow, 2.0 ** -20, "weights")
 
 
-def test_route_topk_workload5_full():
+def test_route_topk_32768_tokens_top8_of_64_full():
     inp = workloads.layer_inputs("cuda:0")
     lg = inp["logits"]
     ids, w = mxa.route_topk(lg, inp["topk"])

@@ -173,11 +173,11 @@ def quant_tensor(cfg, rows, cols, zero_p=0.01, sub_p=0.01, outlier_p=0.001, chun
     return x
 
 
-LAYER5 = {"T": 32768, "H": 7168, "F": 2048, "E": 64, "topk": 8}
 
 
 def layer_inputs(device="cuda:0", seed=5, T=32768, H=7168, F=2048, E=64, topk=8):
-    """Workload-5 inputs drawn on the GPU with a seeded torch generator (the
+    """SwiGLU layer inputs (T=32768 tokens, hidden 7168, ffn 2048, top-8 of 64
+    experts by default) drawn on the GPU with a seeded torch generator (the
     weights alone are 5.6 G elements): router logits fp32 N(0,1) [T, E]; X
     and dOut bf16 N(0,1) [T, H]; W1 [E, 2F, H] (gate rows then up rows) and
     W2 [E, H, F] bf16 0.02 * N(0,1).  Samples are fp32, scaled, then rounded
