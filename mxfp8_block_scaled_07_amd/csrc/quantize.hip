@@ -78,15 +78,18 @@ struct SrcGather {
 };
 
 // ---------------------------------------------------------------------------
-// Dequantize: one thread = 16 codes (one half block); 256 threads = 4 rows x
-// 64 chunks.  grid.x: rows / 4, grid.y: column chunks / 64.
+// Dequantize: one thread = 16 codes (half a block), 256 threads per block over
+// consecutive 16-code chunks of the row-major tensor (rows run into each
+// other, so every block reads and writes one contiguous stretch).
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                                  int64_t rows, int64_t cols, uint16_t* __restrict__ y) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t ch = (int64_t)blockIdx.y * 64 + (threadIdx.x & 63);
-  if (row >= rows || ch >= (cols >> 4)) return;
-  const uint4 c = *reinterpret_cast<const uint4*>(q + row * cols + ch * 16);
+  const int64_t cpr = cols >> 4;  // chunks per row
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= rows * cpr) return;
+  const int64_t row = g / cpr;
+  const int64_t ch = g - row * cpr;
+  const uint4 c = *reinterpret_cast<const uint4*>(q + g * 16);
   const uint32_t sb = s[scale_index(rows, row, ch >> 1)];
   uint4 o0, o1;
   if (sb == 255u) {  // E8M0 NaN scale: the whole block is NaN
@@ -99,7 +102,7 @@ __global__ void __launch_bounds__(256) k_dequant(const uint8_t* __restrict__ q, 
     p = cvt4_bf16(c.z, sc); o1.x = p.x; o1.y = p.y;
     p = cvt4_bf16(c.w, sc); o1.z = p.x; o1.w = p.y;
   }
-  uint16_t* dst = y + row * cols + ch * 16;
+  uint16_t* dst = y + g * 16;
   *reinterpret_cast<uint4*>(dst) = o0;
   *reinterpret_cast<uint4*>(dst + 8) = o1;
 }
@@ -138,9 +141,10 @@ extern "C" int mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, i
                              mx_stream_t stream) {
   if (!q || !s || !y || rows < 0 || cols <= 0 || cols % 32) return MX_EINVAL;
   if (rows == 0) return MX_OK;
-  const dim3 grid((unsigned)((rows + 3) / 4), (unsigned)((cols / 16 + 63) / 64));
-  if ((rows + 3) / 4 > 0x7FFFFFFF || grid.y > 65535u) return MX_EINVAL;
-  hipLaunchKernelGGL(k_dequant, grid, dim3(256), 0, reinterpret_cast<hipStream_t>(stream), q, s, rows, cols, y);
+  const int64_t blocks = (rows * (cols / 16) + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return MX_EINVAL;
+  hipLaunchKernelGGL(k_dequant, dim3((unsigned)blocks), dim3(256), 0, reinterpret_cast<hipStream_t>(stream), q, s,
+                     rows, cols, y);
   return launch_status();
 }
 
