@@ -169,6 +169,7 @@ struct OutTile {
   int64_t ldc, m0, n0, n_end;
   int32_t rows;   // valid output rows
   int32_t steps;
+  int32_t blk_lo, blk_hi;   // valid 32-blocks of the contraction, counted from k_begin
 };
 
 // Tile coordinates of logical tile L.
@@ -289,6 +290,8 @@ __device__ __forceinline__ OutTile out_tile(const Problem& p, const Coord& c) {
   o.n0 = c.row_b;
   o.rows = c.rows_a;
   o.steps = c.steps;
+  o.blk_lo = (c.k_lo - c.k_begin) >> 5;
+  o.blk_hi = (c.k_hi - c.k_begin) >> 5;
   return o;
 }
 
@@ -396,8 +399,11 @@ __device__ __forceinline__ LoadPlan plan_loads(const Loader& ld, const LaneLoads
   pl.as = ld.t.as;
   pl.bs = ld.t.bs;
   pl.soff = ld.valid ? (uint32_t)k0 : 0u;
-  pl.sa = (ld.valid & (ll.srow < ld.t.rows_a)) ? 4u * (uint32_t)ll.srow : kOob;
-  pl.sb = (ld.valid & (ll.srow < ld.t.rows_b)) ? 4u * (uint32_t)ll.srow : kOob;
+  // a step with no valid k (ring padding) reads no scales: its panel offset
+  // may lie past the scale tensor
+  const bool kin = ld.valid & (k0 < ld.t.k_hi) & (k0 + BK > ld.t.k_lo);
+  pl.sa = (kin & (ll.srow < ld.t.rows_a)) ? 4u * (uint32_t)ll.srow : kOob;
+  pl.sb = (kin & (ll.srow < ld.t.rows_b)) ? 4u * (uint32_t)ll.srow : kOob;
   pl.pa = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_a : 0u;
   pl.pb = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_b : 0u;
   pl.dst = lds_addr(stage) + (uint32_t)(4 * w * 1024);
@@ -476,7 +482,12 @@ __device__ __forceinline__ void read_b(const uint8_t* st, Frags& f, int wn, cons
   }
 }
 
-__device__ __forceinline__ uint32_t shr(int v, int sel) { return (uint32_t)v >> sel; }
+// The E8M0 byte a lane passes to the MFMA (bits 7:0 of the operand): byte
+// sel / 8 of the panel dword, or 0 (2^-127, applied to zero codes) when the
+// width is 0.
+__device__ __forceinline__ int scale_byte(int v, int sel, uint32_t width) {
+  return (int)__builtin_amdgcn_ubfe((uint32_t)v, (uint32_t)sel, width);
+}
 
 // MFMAs of A fragments i0, i0 + 1 against the 4 B fragments.
 __device__ __forceinline__ void mma_half(const Frags& f, v16f (&acc)[4][4], int i0) {
@@ -648,8 +659,14 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   uint8_t* const lst = CUR == 0 ? s3 : CUR == 1 ? s0 : CUR == 2 ? s1 : s2;   // stage of step s+3
   uint8_t* const cst = CUR == 0 ? s0 : CUR == 1 ? s1 : CUR == 2 ? s2 : s3;   // stage of step s
   const int h = (threadIdx.x >> 5) & 1;
-  // the step's scale bytes: byte 2 * (k step parity) + h of the panel dword
+  // the step's scale bytes: byte 2 * (k step parity) + h of the panel dword.
+  // Blocks outside the tile's contraction range load zero codes; their scale
+  // bytes are replaced by 0: a wgrad panel can hold blocks of the
+  // neighbouring groups, and a NaN scale (0xFF) of another group must not
+  // reach this group's sums.
   const int sel = 8 * (2 * (c.s & 1) + h);
+  const int32_t bi = 2 * c.s + h;
+  const uint32_t bok = (bi >= c.t.blk_lo) & (bi < c.t.blk_hi) ? 8u : 0u;
   const LoadPlan pl = plan_loads(ld, ll, lst, pa, pb);
   const uint8_t* A = cst + wm * 128 * BK;
   const uint8_t* SA = cst + kScaleOff + wm * 128 * 4;
@@ -658,9 +675,9 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   const uint8_t* nB = nst + kCodeBytes + wn * 128 * BK;
   const uint8_t* nSB = nst + kScaleOff + BM * 4 + wn * 128 * 4;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cur.sb[j] = (int)shr(cur.sb[j], sel);
-  cur.sa[0] = (int)shr(cur.sa[0], sel);
-  cur.sa[1] = (int)shr(cur.sa[1], sel);
+  for (int j = 0; j < 4; ++j) cur.sb[j] = scale_byte(cur.sb[j], sel, bok);
+  cur.sa[0] = scale_byte(cur.sa[0], sel, bok);
+  cur.sa[1] = scale_byte(cur.sa[1], sel, bok);
   __builtin_amdgcn_sched_barrier(0);
 #define MX_MFMA(i, j)                                                                                        \
   acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0, cur.sb[j], \
@@ -679,8 +696,8 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   // stage s+1 complete: own loads, then everyone's
   stage_barrier<kVm>();
   MX_FENCE
-  cur.sa[2] = (int)shr(cur.sa[2], sel);
-  cur.sa[3] = (int)shr(cur.sa[3], sel);
+  cur.sa[2] = scale_byte(cur.sa[2], sel, bok);
+  cur.sa[3] = scale_byte(cur.sa[3], sel, bok);
   // second half: MFMAs of A fragments 2, 3; loads 5..9; the next step's B
   // fragments and A fragments 0, 1
   MX_MFMA(2, 0) load_n(pl, 5); nxt.b[0] = frag(nB, fo);            nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc);       MX_FENCE

@@ -148,6 +148,36 @@ def test_edge_shapes_wgrad(lens, N, K):
         check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, dt)
 
 
+def test_wgrad_nan_block_stays_in_its_group():
+    """A NaN block (scale byte 0xFF) in one group's rows of dY^T or X^T makes
+    only that group's matching dW row or column NaN: the groups that share its
+    128-row scale panel are unaffected (groups start at multiples of 32)."""
+    g = np.random.default_rng(31)
+    off = np.array([0, 96, 224, 320])
+    E, cap, N, K = 3, 352, 64, 96
+    dyt_q, dyt_s = mx_rows(g, (N, cap), 1.0, 0.01)
+    xt_q, xt_s = mx_rows(g, (K, cap))
+    dyt_s[5, 2] = 0xFF    # rows 64..95: group 0, panel 0 shared with group 1
+    dyt_s[9, 7] = 0xFF    # rows 224..255: group 2, panel 1 shared with group 1
+    xt_s[3, 3] = 0xFF     # rows 96..127: group 1, panel 0 shared with group 0
+    nan = np.zeros((E, N, K), bool)
+    nan[0, 5, :] = True
+    nan[2, 9, :] = True
+    nan[1, :, 3] = True
+    C, S = og.grouped_gemm_wgrad(dyt_q, dyt_s, xt_q, xt_s, off)
+    assert np.all(np.isnan(C[nan])) and np.all(np.isfinite(C[~nan]))
+    dw = torch.full((E, N, K), 7.0, dtype=torch.float32, device="cuda:0")
+    mxa.mx_grouped_gemm_wgrad(dev(dyt_q), dev(spanels(dyt_s)), dev(xt_q), dev(spanels(xt_s)),
+                              dev(off.astype(np.int32)), E, cap, N, K, dw, mxa.MX_OUT_F32)
+    torch.cuda.synchronize()
+    got = host(dw).astype(np.float64)
+    assert np.all(np.isnan(got[nan]))
+    got[nan] = C[nan] = S[nan] = 0.0
+    res = tolerance.check(got, C, S, h_fn=wgrad_h_fn(dyt_q, dyt_s, xt_q, xt_s, off, N, K))
+    print("wgrad nan", res)
+    assert res["ok"], res
+
+
 def test_gemm_deterministic():
     g = np.random.default_rng(5)
     a_q, a_s = mx_rows(g, (256, 512))
