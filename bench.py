@@ -133,12 +133,28 @@ def gpu_expert_path(args, c):
         stages[n]["traffic"] = None if tr is None else tr["bytes"]
     gemm_total = sum(work["gemm_flops"].values())
     value = gemm_total / (step_ms * 1e-3) / 1e12
+    # the same step with the quantize fused into the permute (same bytes out)
+    f_ms, f_per, _ = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), moe.FUSED_STAGES, args.steps,
+                                 args.warmup)
+    fused_stages = {}
+    for n in moe.FUSED_STAGES:
+        if n in work["gemm_flops"]:
+            fused_stages[n] = {"ms": round(f_per[n], 4),
+                               "tflops": round(work["gemm_flops"][n] / (f_per[n] * 1e-3) / 1e12, 1)}
+        else:
+            fused_stages[n] = {"ms": round(f_per[n], 4),
+                               "gbps": round(work["bytes"][n] / (f_per[n] * 1e-3) / 1e9, 1)}
+    fused = {"ms_per_step": round(f_ms, 4), "tflops": round(gemm_total / (f_ms * 1e-3) / 1e12, 1),
+             "stages": fused_stages,
+             "note": "routing metadata + one gathered row+col quantize of the bf16 tokens replace quant_x, "
+                     "the MXFP8 permute and quant_xt; bit-identical results"}
     dom = max(work["gemm_flops"], key=lambda n: per[n])
     dom_tf = work["gemm_flops"][dom] / (per[dom] * 1e-3) / 1e12
     counts = np.bincount(c["expert_ids"].ravel(), minlength=E)
     tr = measured_traffic(dom)
     result = {
         "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
+        "fused_quant_permute": fused,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4),
                      "traffic": None if tr is None else tr["bytes"],
@@ -312,7 +328,7 @@ def main():
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the expert path has no multi-GPU leg in this build "
+        print("bench.py measures one GPU: the expert path has no multi-GPU leg "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     ensure_built()
@@ -324,6 +340,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
         "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
+        "fused_quant_permute": res["fused_quant_permute"],
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)

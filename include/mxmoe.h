@@ -61,7 +61,7 @@ typedef void* mx_stream_t; /* a hipStream_t */
 enum {
   MX_OK = 0,
   MX_EINVAL = -1,       /* a null pointer, a bad size or alignment, a bad dtype */
-  MX_EUNSUPPORTED = -2, /* a valid request this build does not implement */
+  MX_EUNSUPPORTED = -2, /* a valid request outside the sizes this library implements */
   MX_EHIP = -3          /* the HIP runtime reported an error at launch */
 };
 

@@ -27,6 +27,15 @@ from . import (MX_OUT_BF16, MX_OUT_F32, mx_combine, mx_combine_bwd_quantize, mx_
 
 STAGES = ("quant_x", "permute", "quant_w", "gemm_fwd", "quant_dy", "gemm_dgrad", "quant_xt", "gemm_wgrad")
 
+# The same computation with the quantize fused into the permute (PR #3203
+# "Next steps" lists fusing the cast and the token shuffle): routing metadata
+# only, then one gathered pass over the bf16 tokens that writes the permuted
+# rowwise MX (GEMM fwd operand) and the columnwise MX in permuted order (wgrad
+# operand).  Rowwise quantization is per row, so quantize-then-permute and
+# permute-then-quantize give the same bytes; the MXFP8 permute stays the step
+# of choice when the token shuffle is a transfer between devices.
+FUSED_STAGES = ("route", "quant_xperm", "quant_w", "gemm_fwd", "quant_dy", "gemm_dgrad", "gemm_wgrad")
+
 
 class ExpertBuffers:
     """Device buffers for one (T, K, N, E, topk) problem, allocated once."""
@@ -72,6 +81,10 @@ def run_stage(name, b, x, w, dy, expert_ids, stream=None):
         mx_grouped_gemm_dgrad(b.dyq, b.dys, b.wtq, b.wtsc, b.off, E, cap, K, N, b.dx, od, stream)
     elif name == "quant_xt":
         mx_quantize(x, 1, T, K, b.src, cap, None, None, b.xtq, b.xts, stream)
+    elif name == "route":
+        mx_permute(None, None, T, K, expert_ids, topk, E, cap, None, None, b.off, b.dst, b.src, b.ws, b.wsb, stream)
+    elif name == "quant_xperm":
+        mx_quantize(x, 1, T, K, b.src, cap, b.xpq, b.xps, b.xtq, b.xts, stream)
     elif name == "gemm_wgrad":
         mx_grouped_gemm_wgrad(b.dytq, b.dyts, b.xtq, b.xts, b.off, E, cap, N, K, b.dw, od, stream)
     else:
@@ -81,6 +94,13 @@ def run_stage(name, b, x, w, dy, expert_ids, stream=None):
 def expert_step(b, x, w, dy, expert_ids, stream=None):
     """One forward + backward pass of the expert computation."""
     for name in STAGES:
+        run_stage(name, b, x, w, dy, expert_ids, stream)
+
+
+def fused_expert_step(b, x, w, dy, expert_ids, stream=None):
+    """The same pass with the quantize fused into the permute (FUSED_STAGES);
+    leaves b.xq / b.xs (the unpermuted rowwise MX) unwritten."""
+    for name in FUSED_STAGES:
         run_stage(name, b, x, w, dy, expert_ids, stream)
 
 
@@ -113,6 +133,8 @@ def algorithmic_work(T, K, N, E, topk, m_real=None):
             "quant_w": rowcol_b(E * N, K),
             "quant_dy": rowcol_b(cap, N),
             "quant_xt": M * K * 2 + cap * K * (1 + 1 / 32) + 4 * cap,
+            "route": 4 * (T * topk * 2 + cap),
+            "quant_xperm": M * K * 2 + 2 * cap * K * (1 + 1 / 32) + 4 * cap,
         },
     }
 

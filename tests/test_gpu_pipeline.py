@@ -141,3 +141,25 @@ def test_expert_step_full_size(case, out_dtype):
     # empty experts: exact zeros
     for e in empty:
         assert torch.count_nonzero(b.dw[e]) == 0
+
+
+def test_fused_quantize_permute_matches_full_path(case):
+    """The step with the quantize fused into the permute (one gathered pass
+    over the bf16 tokens) writes the same bytes as the full path: routing,
+    the permuted rowwise MX, the columnwise MX in permuted order, and the
+    three GEMM outputs (rows inside the groups)."""
+    c, x, w, ids, dy, dy_np, (counts, off, dst, src) = case
+    T, K, N, E, topk = c["T"], c["K"], c["N"], c["E"], c["topk"]
+    a = moe.ExpertBuffers(T, K, N, E, topk)
+    f = moe.ExpertBuffers(T, K, N, E, topk)
+    moe.expert_step(a, x, w, dy, ids)
+    moe.fused_expert_step(f, x, w, dy, ids)
+    torch.cuda.synchronize()
+    hi = int(off[-1])
+    for name in ("off", "dst", "src", "xtq", "xts", "wq", "wsc", "dytq", "dyts"):
+        assert torch.equal(getattr(a, name), getattr(f, name)), name
+    assert torch.equal(a.xpq[:hi], f.xpq[:hi])
+    assert np.array_equal(srows(a.xps, K)[:hi], srows(f.xps, K)[:hi])
+    for name in ("y", "dx"):
+        assert torch.equal(getattr(a, name)[:hi].view(torch.int16), getattr(f, name)[:hi].view(torch.int16)), name
+    assert torch.equal(a.dw.view(torch.int16), f.dw.view(torch.int16))
