@@ -249,6 +249,14 @@ def gpu_swiglu_layer(args):
                        "weights, MXFP8 GEMM operands, bf16 GEMM outputs",
            "steps": steps, "ms_per_step": round(step_ms, 3), "gemm_tflop_per_step": round(flops / 1e12, 3),
            "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4), "stages": stages}
+    # the same layer with the quantize fused into the permute (same bytes out)
+    f_ms, f_per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, logits, dout),
+                                 moe.LAYER_FUSED_STAGES, steps, 2)
+    res["fused_quant_permute"] = {
+        "ms_per_step": round(f_ms, 3), "tflops": round(flops / (f_ms * 1e-3) / 1e12, 1),
+        "stages": {n: {"ms": round(f_per[n], 4), "gbps": round(work["bytes"][n] / (f_per[n] * 1e-3) / 1e9, 1)}
+                   for n in ("route", "quant_xperm")},
+        "replaces": {n: round(per[n], 4) for n in ("quant_x", "permute", "quant_xt")}}
     del b, x, dout, w1, w2, logits
     torch.cuda.empty_cache()
     return res

@@ -148,6 +148,10 @@ def algorithmic_work(T, K, N, E, topk, m_real=None):
 LAYER_STAGES = ("router", "quant_x", "permute", "quant_w1", "gemm1_fwd", "swiglu", "quant_w2", "gemm2_fwd",
                 "combine", "combine_bwd", "router_bwd", "gemm2_dgrad", "gemm2_wgrad", "swiglu_bwd", "gemm1_dgrad",
                 "quant_xt", "gemm1_wgrad", "unpermute_dx")
+# the same layer with the quantize fused into the permute (as FUSED_STAGES)
+LAYER_FUSED_STAGES = ("router", "route", "quant_xperm", "quant_w1", "gemm1_fwd", "swiglu", "quant_w2", "gemm2_fwd",
+                      "combine", "combine_bwd", "router_bwd", "gemm2_dgrad", "gemm2_wgrad", "swiglu_bwd",
+                      "gemm1_dgrad", "gemm1_wgrad", "unpermute_dx")
 
 
 class LayerBuffers:
@@ -200,6 +204,10 @@ def run_layer_stage(name, b, x, w1, w2, logits, dout, stream=None):
         mx_quantize(x, 1, T, H, None, T, b.xq, b.xs, None, None, stream)
     elif name == "permute":
         mx_permute(b.xq, b.xs, T, H, ids, k, E, cap, b.xpq, b.xps, b.off, b.dst, b.src, b.ws, b.wsb, stream)
+    elif name == "route":
+        mx_permute(None, None, T, H, ids, k, E, cap, None, None, b.off, b.dst, b.src, b.ws, b.wsb, stream)
+    elif name == "quant_xperm":
+        mx_quantize(x, 1, T, H, b.src, cap, b.xpq, b.xps, b.xtq, b.xts, stream)
     elif name == "quant_w1":
         mx_quantize(w1, E, 2 * F, H, None, 2 * F, b.w1q, b.w1s, b.w1tq, b.w1ts, stream)
     elif name == "gemm1_fwd":
@@ -241,6 +249,13 @@ def layer_step(b, x, w1, w2, logits, dout, stream=None):
         run_layer_stage(name, b, x, w1, w2, logits, dout, stream)
 
 
+def fused_layer_step(b, x, w1, w2, logits, dout, stream=None):
+    """The same pass with the quantize fused into the permute
+    (LAYER_FUSED_STAGES); leaves b.xq / b.xs unwritten."""
+    for name in LAYER_FUSED_STAGES:
+        run_layer_stage(name, b, x, w1, w2, logits, dout, stream)
+
+
 def layer_work(T, H, F, E, topk):
     """FLOPs of the six GEMMs (real routed rows only) and the algorithmic
     bytes of every other stage (each tensor read or written once)."""
@@ -273,6 +288,8 @@ def layer_work(T, H, F, E, topk):
             "combine_bwd": T * H * 2 + cap * H * 2 * mx + M * 8 + cap * 4,
             "swiglu_bwd": cap * F * 6 + cap * 2 * F * 2 * mx,       # read g, u, dA; write dH row + col MX
             "quant_xt": M * H * 2 + cap * H * mx + 4 * cap,
+            "route": 4 * (M * 2 + cap),
+            "quant_xperm": M * H * 2 + 2 * cap * H * mx + 4 * cap,
             "unpermute_dx": T * H * (2 * topk + 2) + M * 4,
         },
     }

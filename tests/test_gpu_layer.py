@@ -259,3 +259,26 @@ def test_swiglu_backward_and_gate_up_backward(layer):
     res = tolerance.check_bf16_elementwise(rows(b.dx, ts), ex, S)
     print("unpermute_dx", res)
     assert res["ok"], res
+
+
+def test_fused_layer_matches_full_path():
+    """The layer step with the quantize fused into the permute writes the same
+    bytes as the full path (top-8 of 64 experts, reduced sizes): routing,
+    the permuted rowwise MX and columnwise MX of X, the layer output and the
+    gradients of X, W1, W2 and the router logits."""
+    inp = workloads.layer_inputs("cuda:0", T=2048, H=512, F=256, E=64, topk=8)
+    T, H, F, E, k = inp["T"], inp["H"], inp["F"], inp["E"], inp["topk"]
+    a = moe.LayerBuffers(T, H, F, E, k)
+    f = moe.LayerBuffers(T, H, F, E, k)
+    args = (inp["x"], inp["w1"], inp["w2"], inp["logits"], inp["dout"])
+    moe.layer_step(a, *args)
+    moe.fused_layer_step(f, *args)
+    torch.cuda.synchronize()
+    hi = int(a.off[-1])
+    for name in ("ids", "weights", "off", "dst", "src", "xtq", "xts", "out", "dx", "dw1", "dw2", "dlogits"):
+        ta, tf = getattr(a, name), getattr(f, name)
+        if ta.dtype in (torch.bfloat16, torch.float32):
+            ta, tf = ta.view(torch.int16 if ta.dtype == torch.bfloat16 else torch.int32), \
+                tf.view(torch.int16 if tf.dtype == torch.bfloat16 else torch.int32)
+        assert torch.equal(ta, tf), name
+    assert torch.equal(a.xpq[:hi], f.xpq[:hi])
