@@ -26,6 +26,9 @@ namespace {
 // experts) would grow, so large expert counts use larger tiles.
 inline int32_t route_tile(int32_t num_experts) { return num_experts <= 1024 ? 512 : 4096; }
 
+// The routing kernels keep one int32 per expert in LDS (64 KB at most).
+constexpr int32_t kMaxExperts = 16384;
+
 __global__ void __launch_bounds__(256) k_route_hist(const int32_t* __restrict__ ids, int64_t n, int32_t E,
                                                     int32_t tile, int32_t* __restrict__ hist) {
   extern __shared__ int32_t lh[];
@@ -186,7 +189,8 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
                           int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
                           size_t workspace_bytes, mx_stream_t stream) {
   const bool copy = q || s || q_out || s_out;
-  if (tokens < 0 || topk < 1 || num_experts < 1 || num_experts > 65536) return MX_EINVAL;
+  if (tokens < 0 || topk < 1 || num_experts < 1) return MX_EINVAL;
+  if (num_experts > kMaxExperts) return MX_EUNSUPPORTED;
   if (!group_offsets || !src_row || (tokens > 0 && (!expert_ids || !dst_row))) return MX_EINVAL;
   if (copy && (!q || !s || !q_out || !s_out || cols <= 0 || cols % 32)) return MX_EINVAL;
   if (copy && (((uintptr_t)s | (uintptr_t)s_out) & 3)) return MX_EINVAL;  // scale dwords
@@ -199,8 +203,7 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (nt > 0x7FFFFFFF) return MX_EINVAL;
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* base = hist + nt * num_experts;
-  const size_t lds = (size_t)num_experts * sizeof(int32_t);
-  if (lds > 64 * 1024) return MX_EINVAL;
+  const size_t lds = (size_t)num_experts * sizeof(int32_t);  // <= 64 KB (kMaxExperts)
   if (n > 0) {
     hipLaunchKernelGGL(k_route_hist, dim3((unsigned)nt), dim3(256), lds, st, expert_ids, n, num_experts, tile, hist);
   } else {

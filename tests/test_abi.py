@@ -75,6 +75,10 @@ def test_permute_validation(lib):
     # copy requested with a missing output
     assert p(P, P, 100, 64, P, 2, 4, 400, None, P, P, P, P, P, ws, None) == mxa.MX_EINVAL
     assert p(None, None, 100, 0, P, 0, 4, 400, None, None, P, P, P, P, ws, None) == mxa.MX_EINVAL   # topk 0
+    # more experts than the routing kernels hold in LDS: a valid request this library does not implement
+    E = 16385
+    wsb = lib.mx_permute_workspace_size(100, 2, E)
+    assert p(None, None, 100, 0, P, 2, E, 200 + 31 * E, None, None, P, P, P, P, wsb, None) == mxa.MX_EUNSUPPORTED
 
 
 def test_gemm_validation(lib):

@@ -148,6 +148,26 @@ def test_edge_shapes_wgrad(lens, N, K):
         check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, dt)
 
 
+def test_max_groups_fwd_and_wgrad():
+    """2048 groups, the most one call takes, most of them tiny or empty:
+    forward over ragged groups of 0 to 64 rows, wgrad over groups of 0, 32
+    or 64 rows; both compared in full."""
+    g = np.random.default_rng(2048)
+    E, N, K = 2048, 64, 96
+    sizes = g.choice([0, 0, 1, 17, 32, 45, 64], E)
+    ids = workloads.ids_from_sizes(sizes)
+    counts, off, dst, src = routing.route(ids, E)
+    a_q, a_s = routing.permute(*mx_rows(g, (int(sizes.sum()), K), 1.0, 0.01), src)
+    b_q, b_s = mx_rows(g, (E * N, K), 0.02)
+    b_q, b_s = b_q.reshape(E, N, K), b_s.reshape(E, N, K // 32)
+    check_rows("fwd", a_q, a_s, b_q, b_s, off, mxa.MX_OUT_F32)
+    woff = np.concatenate([[0], np.cumsum(g.choice([0, 32, 64], E))])
+    cap = int(woff[-1]) + 32
+    dyt_q, dyt_s = mx_rows(g, (N, cap), 1.0, 0.01)
+    xt_q, xt_s = mx_rows(g, (K, cap))
+    check_wgrad(dyt_q, dyt_s, xt_q, xt_s, woff, mxa.MX_OUT_F32)
+
+
 def test_wgrad_nan_block_stays_in_its_group():
     """A NaN block (scale byte 0xFF) in one group's rows of dY^T or X^T makes
     only that group's matching dW row or column NaN: the groups that share its

@@ -60,7 +60,9 @@ def test_top8_of_64_routing():
     check_permute(c["expert_ids"], 64, K=256, seed=5)
 
 
-@pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 3, 2), (63, 2, 7), (4097, 1, 3), (3000, 2, 300), (100, 4, 1)])
+@pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 3, 2), (63, 2, 7), (4097, 1, 3), (3000, 2, 300), (100, 4, 1),
+                                      (5000, 2, 2048),      # above 1024 experts: 4096-pair routing tiles
+                                      (3000, 1, 16384)])    # the largest expert count (most experts empty)
 def test_edge_shapes(T, topk, E):
     g = np.random.default_rng(T * 7 + E)
     ids = g.integers(0, E, (T, topk))
