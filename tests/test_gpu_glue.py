@@ -115,7 +115,8 @@ def routed(g, T, E, topk, dup=False):
 
 
 @pytest.mark.parametrize("T,H,E,topk,dup", [(300, 96, 6, 2, False), (128, 2048, 16, 8, False),
-                                            (77, 544, 4, 3, True), (64, 32, 3, 1, False), (40, 160, 64, 9, False)])
+                                            (77, 544, 4, 3, True), (64, 32, 3, 1, False), (40, 160, 64, 9, False),
+                                            (50, 96, 128, 64, False)])   # top-64, the router's largest k
 def test_combine(T, H, E, topk, dup):
     g = np.random.default_rng(T * H + topk)
     ids, w, off, dst, src = routed(g, T, E, topk, dup)
@@ -123,13 +124,16 @@ def test_combine(T, H, E, topk, dup):
     y = workloads.normal_bf16(g, (rows, H), 1.0, outlier_p=0.01)
     out = host(mxa.combine(dev(y), dev(dst), dev(w), T, topk))
     exact, S = glue.combine(y, dst, w, topk)
-    res = tolerance.check_bf16_elementwise(out, exact, S)
+    # k fused multiply-adds in j order: at most k fp32 roundings of the
+    # magnitude sum (the default glue bound covers k <= 8)
+    rel = max(tolerance.GLUE_REL, 2.0 * topk * 2.0 ** -24)
+    res = tolerance.check_bf16_elementwise(out, exact, S, rel)
     print("combine", res)
     assert res["ok"], res
     # unweighted: the backward of the permute
     out1 = host(mxa.combine(dev(y), dev(dst), None, T, topk))
     exact1, S1 = glue.combine(y, dst, None, topk)
-    assert tolerance.check_bf16_elementwise(out1, exact1, S1)["ok"]
+    assert tolerance.check_bf16_elementwise(out1, exact1, S1, rel)["ok"]
 
 
 def test_combine_top1_unit_weight_is_exact_unpermute():
@@ -145,7 +149,8 @@ def test_combine_top1_unit_weight_is_exact_unpermute():
 
 
 @pytest.mark.parametrize("T,H,E,topk,dup", [(300, 96, 6, 2, False), (128, 2048, 16, 8, False),
-                                            (77, 544, 4, 3, True), (40, 160, 64, 9, False)])
+                                            (77, 544, 4, 3, True), (40, 160, 64, 9, False),
+                                            (50, 96, 128, 64, False)])
 def test_combine_bwd_quantize(T, H, E, topk, dup):
     g = np.random.default_rng(T + H + topk)
     ids, w, off, dst, src = routed(g, T, E, topk, dup)
