@@ -14,12 +14,17 @@ Printed: one JSON line.  ``value`` = GEMM FLOPs of a step (3 x 2*M*N*K over
 the real routed rows) / step time, in TFLOP/s.  ``stages`` gives each stage's
 mean duration (HIP events on the launch stream, every timed step) and its
 throughput against the MI355X peak (MXFP8 dense 5.0 PFLOP/s, HBM 8 TB/s).
-``roofline`` reports the dominant GEMM stage.  ``quantize_bandwidth`` times
+``roofline`` reports the dominant GEMM stage.  ``fused_quant_permute`` times
+the same step with the quantize fused into the permute (routing metadata plus
+one gathered row+col quantize of the bf16 tokens in place of the X quantize,
+the MXFP8 permute and the permuted X columnwise quantize; same bytes out);
+the headline keeps the MXFP8 permute, the step that becomes a transfer
+between devices when experts are sharded.  ``quantize_bandwidth`` times
 the fused rowwise+columnwise quantize and both dequantizes of a
 [16*8192, 5120] bf16 tensor.  ``swiglu_layer`` times the full SwiGLU expert
 FFN layer (64 experts, top-8, 32768 tokens, hidden 7168, ffn 2048) forward
 plus backward, stage by stage, including the router, SwiGLU and combine
-glue.  ``cpu_baseline`` times the oracle on a bounded sample (three
+glue (and its fused-permute variant).  ``cpu_baseline`` times the oracle on a bounded sample (three
 median-sized experts' share of the step).
 """
 
