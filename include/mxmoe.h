@@ -265,6 +265,48 @@ int mx_router_bwd(const uint16_t* dout, const uint16_t* y, int64_t y_rows, int64
                   const int32_t* expert_ids, const float* weights, int64_t tokens, int32_t num_experts, int32_t topk,
                   float* dw, float* dlogits, mx_stream_t stream);
 
+/*
+ * BF16 baseline of the expert step: the same permute and grouped GEMMs with
+ * bf16 operands, so the MXFP8 path can be timed against the BF16 MoE layer
+ * the digest page compares with (Overview and Key Statistics & Figures: the
+ * MoE-layer speedup of MXFP8 over BF16).
+ *
+ * mx_bf16_gather: row gather and/or transpose of bf16 tensors.
+ *   x         bf16 [batch, rows, cols]
+ *   gather    optional int32 [rows_out] (batch must be 1): output row r is
+ *             source row gather[r], or a zero row when gather[r] < 0 or
+ *             >= rows.  Without a gather, output row r is source row r for
+ *             r < rows and zero after (rows_out >= rows).
+ *   out_rows  bf16 [batch, rows_out, cols], or NULL
+ *   out_cols  the same rows transposed, bf16 [batch, cols, rows_out], or NULL
+ * The permute of the BF16 step is mx_permute with NULL tensors (routing
+ * metadata only) followed by this call with gather = src_row.  Requires
+ * cols % 32 == 0, rows_out % 32 == 0, at least one output, 16-byte aligned
+ * buffers.  Bit-exact copies (no arithmetic).
+ */
+int mx_bf16_gather(const uint16_t* x, int64_t batch, int64_t rows, int64_t cols, const int32_t* gather,
+                   int64_t rows_out, uint16_t* out_rows, uint16_t* out_cols, mx_stream_t stream);
+
+/*
+ * BF16 grouped GEMMs: the three NT products of mx_grouped_gemm_fwd / dgrad /
+ * wgrad with bf16 operands (no scales), fp32 accumulation, bf16 (RNE) or
+ * fp32 output; same groups, shapes, limits and pad-row behaviour.
+ *   fwd:   a = X_perm bf16 [m_cap, k], b = W bf16 [E, n, k], out [m_cap, n]
+ *   dgrad: a = dY bf16 [m_cap, n_c], b = W^T bf16 [E, k_o, n_c], out [m_cap, k_o]
+ *   wgrad: a = dY^T bf16 [n, m_cap], b = X_perm^T bf16 [k, m_cap], out [E, n, k]
+ * Operands must be 16-byte aligned.
+ */
+int mx_bf16_grouped_gemm_fwd(const uint16_t* a, const uint16_t* b, const int32_t* group_offsets, int32_t num_groups,
+                             int64_t m_cap, int64_t n, int64_t k, void* out, int32_t out_dtype, mx_stream_t stream);
+
+int mx_bf16_grouped_gemm_dgrad(const uint16_t* dy, const uint16_t* wt, const int32_t* group_offsets,
+                               int32_t num_groups, int64_t m_cap, int64_t n_out, int64_t k_contract, void* dx,
+                               int32_t out_dtype, mx_stream_t stream);
+
+int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const int32_t* group_offsets,
+                               int32_t num_groups, int64_t m_cap, int64_t n, int64_t k, void* dw, int32_t out_dtype,
+                               mx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

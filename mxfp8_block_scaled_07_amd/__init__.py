@@ -38,6 +38,10 @@ _SIGNATURES = {
                                                _vp]),
     "mx_route_topk": (ctypes.c_int, [_vp, _i64, _i32, _i32, _vp, _vp, _vp]),
     "mx_router_bwd": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]),
+    "mx_bf16_gather": (ctypes.c_int, [_vp, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp]),
+    "mx_bf16_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "mx_bf16_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
+    "mx_bf16_grouped_gemm_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
 }
 
 
@@ -144,6 +148,27 @@ def mx_router_bwd(dout, y, y_rows, H, dst_row, expert_ids, weights, tokens, num_
                   stream=None):
     _check(lib().mx_router_bwd(_p(dout), _p(y), y_rows, H, _p(dst_row), _p(expert_ids), _p(weights), tokens,
                                num_experts, topk, _p(dw), _p(dlogits), _s(stream)), "mx_router_bwd")
+
+
+def mx_bf16_gather(x, batch, rows, cols, gather, rows_out, out_rows, out_cols, stream=None):
+    _check(lib().mx_bf16_gather(_p(x), batch, rows, cols, _p(gather), rows_out, _p(out_rows), _p(out_cols),
+                                _s(stream)), "mx_bf16_gather")
+
+
+def mx_bf16_grouped_gemm_fwd(a, b, group_offsets, num_groups, m_cap, n, k, out, out_dtype, stream=None):
+    _check(lib().mx_bf16_grouped_gemm_fwd(_p(a), _p(b), _p(group_offsets), num_groups, m_cap, n, k, _p(out),
+                                          out_dtype, _s(stream)), "mx_bf16_grouped_gemm_fwd")
+
+
+def mx_bf16_grouped_gemm_dgrad(dy, wt, group_offsets, num_groups, m_cap, n_out, k_contract, dx, out_dtype,
+                               stream=None):
+    _check(lib().mx_bf16_grouped_gemm_dgrad(_p(dy), _p(wt), _p(group_offsets), num_groups, m_cap, n_out, k_contract,
+                                            _p(dx), out_dtype, _s(stream)), "mx_bf16_grouped_gemm_dgrad")
+
+
+def mx_bf16_grouped_gemm_wgrad(dyt, xt, group_offsets, num_groups, m_cap, n, k, dw, out_dtype, stream=None):
+    _check(lib().mx_bf16_grouped_gemm_wgrad(_p(dyt), _p(xt), _p(group_offsets), num_groups, m_cap, n, k, _p(dw),
+                                            out_dtype, _s(stream)), "mx_bf16_grouped_gemm_wgrad")
 
 
 # --- allocating helpers ----------------------------------------------------

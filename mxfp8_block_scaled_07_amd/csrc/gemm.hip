@@ -64,6 +64,16 @@ constexpr uint32_t kOob = 0x80000000u;                  // voffset that reads as
 constexpr int kVmem = 10;
 constexpr int kVmemFirst = 5;
 
+// The bf16 baseline runs the same kernel with bf16 operands: a 64-byte LDS
+// row holds 32 bf16, so a k step contracts 32 elements with two
+// V_MFMA_F32_32X32X16_BF16 per 32 x 32 tile (the same MFMA cycles and LDS
+// bytes per step as one scaled FP8 MFMA of 64), and there are no scales.
+template <bool kBf16>
+struct Elt {
+  static constexpr int kBytes = kBf16 ? 2 : 1;          // bytes per operand element
+  static constexpr int kVmem = kBf16 ? 8 : mx::kVmem;   // vector-memory instructions per wave per stage
+};
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
 // bits 15:14, expcnt in 6:4, lgkmcnt in 11:8).
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
@@ -180,7 +190,7 @@ struct Coord {
 
 // (32-bit tile arithmetic: tile counts are below 2^31, checked on the host;
 // 32-bit divisions are much shorter than 64-bit ones)
-template <bool kWgrad>
+template <bool kWgrad, bool kBf16>
 __device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E, int64_t m_tiles, int64_t n_tiles,
                                        int64_t L64) {
   Coord c;
@@ -216,10 +226,11 @@ __device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E,
     c.row_b = (int64_t)nt * BN;
     c.rows_a = (int32_t)(hi - c.row_a < BM ? hi - c.row_a : BM);
     c.rows_b = (int32_t)(p.N - c.row_b < BN ? p.N - c.row_b : BN);
+    // k in bytes of an operand row
     c.k_begin = 0;
     c.k_lo = 0;
-    c.k_hi = (int32_t)p.K;
-    c.steps = (int32_t)((p.K + BK - 1) / BK);
+    c.k_hi = (int32_t)(p.K * Elt<kBf16>::kBytes);
+    c.steps = (int32_t)((p.K * Elt<kBf16>::kBytes + BK - 1) / BK);
   } else {
     // dW_e tiles walked in bands of 4 m tiles, n-tile major inside a band, so
     // concurrently running tiles share A and B rows
@@ -241,22 +252,25 @@ __device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E,
     c.row_b = (int64_t)nt * BN;
     c.rows_a = (int32_t)(p.N - c.row_a < BM ? p.N - c.row_a : BM);
     c.rows_b = (int32_t)(p.K - c.row_b < BN ? p.K - c.row_b : BN);
-    c.k_begin = lo & ~127;
-    c.k_lo = lo;
-    c.k_hi = hi;
-    c.steps = hi > lo ? (hi - c.k_begin + BK - 1) / BK : 0;
+    // k in bytes of an operand row; MX steps start at the group's 128-row
+    // scale panel, bf16 steps at the group's first row
+    constexpr int32_t eb = Elt<kBf16>::kBytes;
+    c.k_begin = kBf16 ? lo * eb : lo & ~127;
+    c.k_lo = lo * eb;
+    c.k_hi = hi * eb;
+    c.steps = hi > lo ? (c.k_hi - c.k_begin + BK - 1) / BK : 0;
   }
   return c;
 }
 
-template <bool kWgrad>
+template <bool kWgrad, bool kBf16>
 __device__ __forceinline__ LoadTile load_tile(const Problem& p, const Coord& c, int E) {
   LoadTile t;
-  const int64_t ld = kWgrad ? p.m_cap : p.K;               // bytes per operand row
+  const int64_t ld = (kWgrad ? p.m_cap : p.K) * Elt<kBf16>::kBytes;  // bytes per operand row
   const int64_t pa = kWgrad ? 4 * p.N : 4 * p.m_cap;      // scale panel strides
   const int64_t pb = kWgrad ? 4 * p.K : 4 * (int64_t)E * p.N;
   const int64_t panels = (ld + 127) >> 7;
-  const uint8_t* bq = kWgrad ? p.b_q : p.b_q + c.e * p.N * p.K;
+  const uint8_t* bq = kWgrad ? p.b_q : p.b_q + c.e * p.N * p.K * Elt<kBf16>::kBytes;
   const uint8_t* bs = kWgrad ? p.b_s : p.b_s + c.e * p.N * 4;
   // num_records: rows past the valid ones read as zero; every span is below
   // 2^31 (checked on the host)
@@ -296,13 +310,13 @@ __device__ __forceinline__ OutTile out_tile(const Problem& p, const Coord& c) {
 }
 
 // Everything needed to walk the workgroup's tiles.
-template <bool kWgrad>
+template <bool kWgrad, bool kBf16>
 struct Walk {
   const Problem& p;
   const Sched& sc;
   int E;
   int64_t m_tiles, n_tiles, stride, L_end;
-  __device__ __forceinline__ Coord at(int64_t L) const { return coord<kWgrad>(p, sc, E, m_tiles, n_tiles, L); }
+  __device__ __forceinline__ Coord at(int64_t L) const { return coord<kWgrad, kBf16>(p, sc, E, m_tiles, n_tiles, L); }
 };
 
 // Per-lane constants of the loads.  Code loads: lane l of wave w writes 16 B
@@ -329,14 +343,14 @@ struct Loader {
   bool valid;
 };
 
-template <bool kWgrad>
-__device__ __forceinline__ void loader_seek(Loader& ld, const Walk<kWgrad>& w) {
+template <bool kWgrad, bool kBf16>
+__device__ __forceinline__ void loader_seek(Loader& ld, const Walk<kWgrad, kBf16>& w) {
   while (ld.valid && ld.s >= ring_steps(ld.t.steps)) {
     ld.L += w.stride;
     if (ld.L >= w.L_end) {
       ld.valid = false;
     } else {
-      ld.t = load_tile<kWgrad>(w.p, w.at(ld.L), w.E);
+      ld.t = load_tile<kWgrad, kBf16>(w.p, w.at(ld.L), w.E);
       ld.s = 0;
     }
   }
@@ -411,12 +425,14 @@ __device__ __forceinline__ LoadPlan plan_loads(const Loader& ld, const LaneLoads
   return pl;
 }
 
-// Load number n (0..9) of a plan.
+// Load number n (0..9) of a plan; the bf16 operands have no scale loads (8, 9).
+template <bool kBf16>
 __device__ __forceinline__ void load_n(const LoadPlan& pl, int n) {
   if (n < 8) {
     const int i = n >> 1;
     if (n & 1) dma16(pl.bq, pl.dst + kCodeBytes + i * 1024, pl.v[i], pl.soff);
     else dma16(pl.aq, pl.dst + i * 1024, pl.v[i], pl.soff);
+  } else if (kBf16) {
   } else if (n == 8) {
     dma4(pl.as, pl.sdst, pl.sa, pl.pa);
   } else {
@@ -424,9 +440,10 @@ __device__ __forceinline__ void load_n(const LoadPlan& pl, int n) {
   }
 }
 
+template <bool kBf16>
 __device__ __forceinline__ void issue_all(const LoadPlan& pl) {
 #pragma unroll
-  for (int n = 0; n < kVmem; ++n) load_n(pl, n);
+  for (int n = 0; n < kVmem; ++n) load_n<kBf16>(pl, n);
 }
 
 // The MFMA operands of one k step for one wave.  Scales hold the raw panel
@@ -487,6 +504,27 @@ __device__ __forceinline__ void read_b(const uint8_t* st, Frags& f, int wn, cons
 // width is 0.
 __device__ __forceinline__ int scale_byte(int v, int sel, uint32_t width) {
   return (int)__builtin_amdgcn_ubfe((uint32_t)v, (uint32_t)sel, width);
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// One k step of one 32 x 32 tile: a scaled FP8 MFMA over 64 k, or for bf16
+// operands two bf16 MFMAs over the lane's two 16-byte chunks (A and B
+// fragments share the lane -> k layout, so the k order of the two halves
+// does not matter).
+template <bool kBf16>
+__device__ __forceinline__ v16f mma(const v8i& b, const v8i& a, const v16f& c, int sb, int sa) {
+  if constexpr (kBf16) {
+    const v8bf b0 = __builtin_bit_cast(v8bf, v4i{b[0], b[1], b[2], b[3]});
+    const v8bf a0 = __builtin_bit_cast(v8bf, v4i{a[0], a[1], a[2], a[3]});
+    const v8bf b1 = __builtin_bit_cast(v8bf, v4i{b[4], b[5], b[6], b[7]});
+    const v8bf a1 = __builtin_bit_cast(v8bf, v4i{a[4], a[5], a[6], a[7]});
+    const v16f t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b0, a0, c, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b1, a1, t, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, c, 0, 0, 0, sb, 0, sa);
+  }
 }
 
 // MFMAs of A fragments i0, i0 + 1 against the 4 B fragments.
@@ -604,8 +642,8 @@ struct Cursor {
 // more younger operations behind the loads they wait for (see kVmAfter).
 // The epilogue stages through LDS stage 3, which the next step's loads
 // overwrite: a barrier after it keeps every wave's reads ahead of them.
-template <bool kF32, bool kWgrad>
-__device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad>& w, v16f (&acc)[4][4], int wm, int wn,
+template <bool kF32, bool kWgrad, bool kBf16>
+__device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad, kBf16>& w, v16f (&acc)[4][4], int wm, int wn,
                                             uint8_t* st3) {
   store_tile<kF32>(c.t, acc, wm, wn, st3);
   zero_acc(acc);
@@ -650,10 +688,10 @@ __device__ __forceinline__ void stage_barrier() {
 //
 // The step is written as 16 slots, one MFMA each, with the loads and LDS
 // reads spread over them; scheduling fences between slots keep that order.
-template <int CUR, int kVm, bool kWgrad>
+template <int CUR, int kVm, bool kWgrad, bool kBf16>
 __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3, Frags& cur, Frags& nxt,
                                        v16f (&acc)[4][4], Loader& ld, const LaneLoads& ll, Cursor& c,
-                                       const Walk<kWgrad>& w, int wm, int wn, int64_t pa, int64_t pb,
+                                       const Walk<kWgrad, kBf16>& w, int wm, int wn, int64_t pa, int64_t pb,
                                        const FragOff& fo) {
   uint8_t* const nst = CUR == 0 ? s1 : CUR == 1 ? s2 : CUR == 2 ? s3 : s0;   // stage of step s+1
   uint8_t* const lst = CUR == 0 ? s3 : CUR == 1 ? s0 : CUR == 2 ? s1 : s2;   // stage of step s+3
@@ -674,21 +712,22 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   const uint8_t* nSA = nst + kScaleOff + wm * 128 * 4;
   const uint8_t* nB = nst + kCodeBytes + wn * 128 * BK;
   const uint8_t* nSB = nst + kScaleOff + BM * 4 + wn * 128 * 4;
+  if constexpr (!kBf16) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cur.sb[j] = scale_byte(cur.sb[j], sel, bok);
-  cur.sa[0] = scale_byte(cur.sa[0], sel, bok);
-  cur.sa[1] = scale_byte(cur.sa[1], sel, bok);
+    for (int j = 0; j < 4; ++j) cur.sb[j] = scale_byte(cur.sb[j], sel, bok);
+    cur.sa[0] = scale_byte(cur.sa[0], sel, bok);
+    cur.sa[1] = scale_byte(cur.sa[1], sel, bok);
+  }
   __builtin_amdgcn_sched_barrier(0);
-#define MX_MFMA(i, j)                                                                                        \
-  acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cur.b[j], cur.a[i], acc[i][j], 0, 0, 0, cur.sb[j], \
-                                                              0, cur.sa[i]);
+#define MX_MFMA(i, j) acc[i][j] = mma<kBf16>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
+#define MX_SCALE(x) if constexpr (!kBf16) { x; }
   // first half: MFMAs of A fragments 0, 1; loads 0..4; A fragments 2, 3
-  MX_MFMA(0, 0) load_n(pl, 0); cur.a[2] = frag(A + 64 * BK, fo);                      MX_FENCE
-  MX_MFMA(0, 1) load_n(pl, 1); cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc); MX_FENCE
-  MX_MFMA(0, 2) load_n(pl, 2); cur.a[3] = frag(A + 96 * BK, fo);                      MX_FENCE
-  MX_MFMA(0, 3) load_n(pl, 3); cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc); MX_FENCE
-  MX_MFMA(1, 0) load_n(pl, 4);                                                        MX_FENCE
+  MX_MFMA(0, 0) load_n<kBf16>(pl, 0); cur.a[2] = frag(A + 64 * BK, fo);                             MX_FENCE
+  MX_MFMA(0, 1) load_n<kBf16>(pl, 1); MX_SCALE(cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc)) MX_FENCE
+  MX_MFMA(0, 2) load_n<kBf16>(pl, 2); cur.a[3] = frag(A + 96 * BK, fo);                             MX_FENCE
+  MX_MFMA(0, 3) load_n<kBf16>(pl, 3); MX_SCALE(cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc)) MX_FENCE
+  MX_MFMA(1, 0) load_n<kBf16>(pl, 4);                                                               MX_FENCE
   MX_MFMA(1, 1)                                                                       MX_FENCE
   MX_MFMA(1, 2)                                                                       MX_FENCE
   MX_MFMA(1, 3)                                                                       MX_FENCE
@@ -696,34 +735,37 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   // stage s+1 complete: own loads, then everyone's
   stage_barrier<kVm>();
   MX_FENCE
-  cur.sa[2] = scale_byte(cur.sa[2], sel, bok);
-  cur.sa[3] = scale_byte(cur.sa[3], sel, bok);
+  if constexpr (!kBf16) {
+    cur.sa[2] = scale_byte(cur.sa[2], sel, bok);
+    cur.sa[3] = scale_byte(cur.sa[3], sel, bok);
+  }
   // second half: MFMAs of A fragments 2, 3; loads 5..9; the next step's B
   // fragments and A fragments 0, 1
-  MX_MFMA(2, 0) load_n(pl, 5); nxt.b[0] = frag(nB, fo);            nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc);       MX_FENCE
-  MX_MFMA(2, 1) load_n(pl, 6); nxt.b[1] = frag(nB + 32 * BK, fo);  nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc); MX_FENCE
-  MX_MFMA(2, 2) load_n(pl, 7); nxt.b[2] = frag(nB + 64 * BK, fo);  nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc); MX_FENCE
-  MX_MFMA(2, 3) load_n(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo);  nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc); MX_FENCE
-  MX_MFMA(3, 0) load_n(pl, 9); nxt.a[0] = frag(nA, fo);            nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc);       MX_FENCE
-  MX_MFMA(3, 1)                nxt.a[1] = frag(nA + 32 * BK, fo);  nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc); MX_FENCE
-  MX_MFMA(3, 2)                                                                                                               MX_FENCE
-  MX_MFMA(3, 3)                                                                                                               MX_FENCE
+  MX_MFMA(2, 0) load_n<kBf16>(pl, 5); nxt.b[0] = frag(nB, fo);           MX_SCALE(nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc))       MX_FENCE
+  MX_MFMA(2, 1) load_n<kBf16>(pl, 6); nxt.b[1] = frag(nB + 32 * BK, fo); MX_SCALE(nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 2) load_n<kBf16>(pl, 7); nxt.b[2] = frag(nB + 64 * BK, fo); MX_SCALE(nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 3) load_n<kBf16>(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo); MX_SCALE(nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc)) MX_FENCE
+  MX_MFMA(3, 0) load_n<kBf16>(pl, 9); nxt.a[0] = frag(nA, fo);           MX_SCALE(nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc))       MX_FENCE
+  MX_MFMA(3, 1)                       nxt.a[1] = frag(nA + 32 * BK, fo); MX_SCALE(nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(3, 2)                                                                                                                      MX_FENCE
+  MX_MFMA(3, 3)                                                                                                                      MX_FENCE
 #undef MX_MFMA
 #undef MX_FENCE
+#undef MX_SCALE
   pin(acc, 2);
   // the next step's fragments are in registers before any wave can pass the
   // next barrier and start overwriting their stage
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_sched_barrier(0);
   ++ld.s;
-  loader_seek<kWgrad>(ld, w);
+  loader_seek<kWgrad, kBf16>(ld, w);
   ++c.s;
 }
 
 // Persistent workgroup: one per CU.  Logical tiles are split into 8 contiguous
 // ranges, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an
 // XCD walk their range round robin.
-template <bool kF32, bool kWgrad>
+template <bool kF32, bool kWgrad, bool kBf16>
 __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __restrict__ offsets, int32_t E) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
@@ -739,11 +781,11 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   const int64_t L_end = (x + 1) * per_xcd < total ? (x + 1) * per_xcd : total;
   const int64_t L0 = x * per_xcd + blockIdx.x / kXcds;
   if (L0 >= L_end) return;
-  const Walk<kWgrad> w{p, sc, E, m_tiles, n_tiles, (int64_t)(gridDim.x / kXcds), L_end};
+  const Walk<kWgrad, kBf16> w{p, sc, E, m_tiles, n_tiles, (int64_t)(gridDim.x / kXcds), L_end};
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int lane = threadIdx.x & 63;
-  const int64_t ldb = kWgrad ? p.m_cap : p.K;
+  const int64_t ldb = (kWgrad ? p.m_cap : p.K) * Elt<kBf16>::kBytes;  // bytes per operand row
   const int64_t pa = kWgrad ? 4 * p.N : 4 * p.m_cap;
   const int64_t pb = kWgrad ? 4 * p.K : 4 * (int64_t)E * p.N;
   LaneLoads ll;
@@ -771,18 +813,18 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   // loader: starts at the same tile; the prologue fills stages 0..2
   Loader ld;
   ld.L = c.L;
-  ld.t = load_tile<kWgrad>(p, w.at(c.L), E);
+  ld.t = load_tile<kWgrad, kBf16>(p, w.at(c.L), E);
   ld.s = 0;
   ld.valid = true;
-  issue_all(plan_loads(ld, ll, st0, pa, pb));
+  issue_all<kBf16>(plan_loads(ld, ll, st0, pa, pb));
   ++ld.s;
-  loader_seek<kWgrad>(ld, w);
-  issue_all(plan_loads(ld, ll, st1, pa, pb));
+  loader_seek<kWgrad, kBf16>(ld, w);
+  issue_all<kBf16>(plan_loads(ld, ll, st1, pa, pb));
   ++ld.s;
-  loader_seek<kWgrad>(ld, w);
-  issue_all(plan_loads(ld, ll, st2, pa, pb));
+  loader_seek<kWgrad, kBf16>(ld, w);
+  issue_all<kBf16>(plan_loads(ld, ll, st2, pa, pb));
   ++ld.s;
-  loader_seek<kWgrad>(ld, w);
+  loader_seek<kWgrad, kBf16>(ld, w);
   // drain the prologue: the first two steps wait with vmcnt(63)
   stage_barrier<0>();
   const FragOff fo = frag_off();
@@ -794,37 +836,37 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   // operations in flight (the loads of s+2 and the first part of s+3).  The
   // first two steps of a tile follow a tile store (or the drained prologue):
   // the tile's stores add tile_stores() younger operations, see finish_tile.
-  constexpr int kSteady = kVmem + kVmemFirst;
+  constexpr int kSteady = Elt<kBf16>::kVmem + kVmemFirst;
   constexpr int kVmAfter = kSteady + tile_stores<kF32>() < 63 ? kSteady + tile_stores<kF32>() : 63;
   do {
-    k_step<0, kVmAfter, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<1, kVmAfter, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<2, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<3, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<0, kVmAfter, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, kVmAfter, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<2, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<3, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
     while (c.s < c.t.steps) {
-      k_step<0, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<1, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<2, kSteady, kWgrad>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<3, kSteady, kWgrad>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<0, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<2, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<3, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
     }
-  } while (finish_tile<kF32, kWgrad>(c, w, acc, wm, wn, st3));
+  } while (finish_tile<kF32, kWgrad, kBf16>(c, w, acc, wm, wn, st3));
   // loads past the last tile may still be writing LDS
   __builtin_amdgcn_s_waitcnt(0);
 }
 
-template <bool kF32, bool kWgrad>
+template <bool kF32, bool kWgrad, bool kBf16>
 void launch(int ctas, hipStream_t st, const Problem& p, const int32_t* off, int32_t E) {
-  hipLaunchKernelGGL((k_gemm<kF32, kWgrad>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
+  hipLaunchKernelGGL((k_gemm<kF32, kWgrad, kBf16>), dim3(ctas), dim3(kThreads), 0, st, p, off, E);
 }
 
-template <bool kWgrad>
+template <bool kWgrad, bool kBf16>
 int launch_any(const Problem& p, const int32_t* off, int32_t E, hipStream_t st) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return MX_EHIP;
   const int ctas = (cus > 0 ? (cus + kXcds - 1) / kXcds : 1) * kXcds;
-  if (p.f32) launch<true, kWgrad>(ctas, st, p, off, E);
-  else launch<false, kWgrad>(ctas, st, p, off, E);
+  if (p.f32) launch<true, kWgrad, kBf16>(ctas, st, p, off, E);
+  else launch<false, kWgrad, kBf16>(ctas, st, p, off, E);
   return launch_status();
 }
 
@@ -848,7 +890,7 @@ static int gemm_rows(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
   if (panels * 4 * m_cap >= (1ll << 31) || panels * 4 * (int64_t)E * N >= (1ll << 31)) return MX_EINVAL;
   if (N >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x N x 4 bytes < 2^31
   const Problem p{a_q, a_s, b_q, b_s, m_cap, N, K, out, out_dtype == MX_OUT_F32};
-  return launch_any<false>(p, offsets, E, reinterpret_cast<hipStream_t>(stream));
+  return launch_any<false, false>(p, offsets, E, reinterpret_cast<hipStream_t>(stream));
 }
 
 extern "C" int mx_grouped_gemm_fwd(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q, const uint8_t* b_s,
@@ -880,5 +922,56 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
   if (panels * 4 * n >= (1ll << 31) || panels * 4 * k >= (1ll << 31)) return MX_EINVAL;
   if (k >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x k x 4 bytes < 2^31
   const Problem p{dyt_q, dyt_s, xt_q, xt_s, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
-  return launch_any<true>(p, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
+  return launch_any<true, false>(p, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// bf16 baseline: the same grouped products with bf16 operands and no scales.
+// Operand rows are 2 * K (or 2 * M_cap) bytes; the scale pointers of the
+// problem are never read (the operand pointers stand in for them).
+
+static int bf16_rows(const uint16_t* a, const uint16_t* b, const int32_t* offsets, int32_t E, int64_t m_cap,
+                     int64_t N, int64_t K, void* out, int32_t out_dtype, mx_stream_t stream) {
+  if (!a || !b || !offsets || !out) return MX_EINVAL;
+  if (((uintptr_t)a | (uintptr_t)b) & 15) return MX_EINVAL;  // 16-byte operand loads
+  if (E < 1 || m_cap < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_EINVAL;
+  if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
+  if ((int64_t)BM * 2 * K >= (1ll << 31) || m_cap >= (1ll << 31)) return MX_EINVAL;  // 32-bit tile spans and bounds
+  if (E > kMaxGroups) return MX_EUNSUPPORTED;
+  if (m_cap == 0) return MX_OK;
+  if (((m_cap + BM - 1) / BM + E) * ((N + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  if (N >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x N x 4 bytes < 2^31
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(a);
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(b);
+  const Problem p{a8, a8, b8, b8, m_cap, N, K, out, out_dtype == MX_OUT_F32};
+  return launch_any<false, true>(p, offsets, E, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int mx_bf16_grouped_gemm_fwd(const uint16_t* a, const uint16_t* b, const int32_t* group_offsets,
+                                        int32_t num_groups, int64_t m_cap, int64_t n, int64_t k, void* out,
+                                        int32_t out_dtype, mx_stream_t stream) {
+  return bf16_rows(a, b, group_offsets, num_groups, m_cap, n, k, out, out_dtype, stream);
+}
+
+extern "C" int mx_bf16_grouped_gemm_dgrad(const uint16_t* dy, const uint16_t* wt, const int32_t* group_offsets,
+                                          int32_t num_groups, int64_t m_cap, int64_t n_out, int64_t k_contract,
+                                          void* dx, int32_t out_dtype, mx_stream_t stream) {
+  return bf16_rows(dy, wt, group_offsets, num_groups, m_cap, n_out, k_contract, dx, out_dtype, stream);
+}
+
+extern "C" int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const int32_t* group_offsets,
+                                          int32_t num_groups, int64_t m_cap, int64_t n, int64_t k, void* dw,
+                                          int32_t out_dtype, mx_stream_t stream) {
+  if (!dyt || !xt || !group_offsets || !dw) return MX_EINVAL;
+  if (((uintptr_t)dyt | (uintptr_t)xt) & 15) return MX_EINVAL;  // 16-byte operand loads
+  if (num_groups < 1 || m_cap < 0 || m_cap % 32 || n <= 0 || k <= 0 || n % 32 || k % 32) return MX_EINVAL;
+  if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
+  if ((int64_t)BM * 2 * m_cap >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile
+  if (num_groups > kMaxGroups) return MX_EUNSUPPORTED;
+  if ((int64_t)num_groups * ((n + BM - 1) / BM) * ((k + BN - 1) / BN) >= (1ll << 31)) return MX_EINVAL;
+  if (k >= (1 << 21)) return MX_EINVAL;  // output tile spans 256 rows x k x 4 bytes < 2^31
+  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(dyt);
+  const uint8_t* b8 = reinterpret_cast<const uint8_t*>(xt);
+  const Problem p{a8, a8, b8, b8, m_cap, n, k, dw, out_dtype == MX_OUT_F32};
+  return launch_any<true, true>(p, group_offsets, num_groups, reinterpret_cast<hipStream_t>(stream));
 }

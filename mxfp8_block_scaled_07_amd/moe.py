@@ -21,7 +21,8 @@ combine backward writes); ``zero_pad_rows`` prepares such a tensor.
 
 import torch
 
-from . import (MX_OUT_BF16, MX_OUT_F32, mx_combine, mx_combine_bwd_quantize, mx_grouped_gemm_dgrad,
+from . import (MX_OUT_BF16, MX_OUT_F32, mx_bf16_gather, mx_bf16_grouped_gemm_dgrad, mx_bf16_grouped_gemm_fwd,
+               mx_bf16_grouped_gemm_wgrad, mx_combine, mx_combine_bwd_quantize, mx_grouped_gemm_dgrad,
                mx_grouped_gemm_fwd, mx_grouped_gemm_wgrad, mx_permute, mx_permute_workspace_size, mx_quantize,
                mx_route_topk, mx_router_bwd, mx_swiglu_bwd_quantize, mx_swiglu_quantize, scale_shape)
 
@@ -102,6 +103,86 @@ def fused_expert_step(b, x, w, dy, expert_ids, stream=None):
     leaves b.xq / b.xs (the unpermuted rowwise MX) unwritten."""
     for name in FUSED_STAGES:
         run_stage(name, b, x, w, dy, expert_ids, stream)
+
+
+# The BF16 baseline of the same step (the digest's Overview compares the
+# MXFP8 MoE layer with a BF16 one): the same routing, the tokens gathered
+# into expert order in bf16, the operands the GEMMs read along the other axis
+# transposed in bf16 (the counterpart of the columnwise quantizes), and the
+# three grouped GEMMs on bf16 operands.
+BF16_STAGES = ("route", "permute_bf16", "transpose_w", "gemm_fwd", "transpose_dy", "gemm_dgrad", "transpose_xt",
+               "gemm_wgrad")
+
+
+class Bf16Buffers:
+    """Device buffers of the BF16 step for one (T, K, N, E, topk) problem."""
+
+    def __init__(self, T, K, N, E, topk, device="cuda:0", out_dtype=MX_OUT_BF16):
+        self.T, self.K, self.N, self.E, self.topk = T, K, N, E, topk
+        self.cap = -(-(T * topk + 31 * E) // 32) * 32
+        self.out_dtype = out_dtype
+        bf, i32 = torch.bfloat16, torch.int32
+        od = torch.bfloat16 if out_dtype == MX_OUT_BF16 else torch.float32
+        cap = self.cap
+        e = lambda *s, dt=bf: torch.empty(s, dtype=dt, device=device)  # noqa: E731
+        self.off, self.dst, self.src = e(E + 1, dt=i32), e(T * topk, dt=i32), e(cap, dt=i32)
+        self.wsb = mx_permute_workspace_size(T, topk, E)
+        self.ws = e(max(self.wsb, 4), dt=torch.uint8)
+        self.xp = e(cap, K)
+        self.wt = e(E, K, N)
+        self.dyt = e(N, cap)
+        self.xt = e(K, cap)
+        self.y = e(cap, N, dt=od)
+        self.dx = e(cap, K, dt=od)
+        self.dw = e(E, N, K, dt=od)
+
+
+def run_bf16_stage(name, b, x, w, dy, expert_ids, stream=None):
+    """Launch one named stage of the BF16 step on ``stream``."""
+    T, K, N, E, topk, cap, od = b.T, b.K, b.N, b.E, b.topk, b.cap, b.out_dtype
+    if name == "route":
+        mx_permute(None, None, T, K, expert_ids, topk, E, cap, None, None, b.off, b.dst, b.src, b.ws, b.wsb, stream)
+    elif name == "permute_bf16":
+        mx_bf16_gather(x, 1, T, K, b.src, cap, b.xp, None, stream)
+    elif name == "transpose_w":
+        mx_bf16_gather(w, E, N, K, None, N, None, b.wt, stream)
+    elif name == "gemm_fwd":
+        mx_bf16_grouped_gemm_fwd(b.xp, w, b.off, E, cap, N, K, b.y, od, stream)
+    elif name == "transpose_dy":
+        mx_bf16_gather(dy, 1, cap, N, None, cap, None, b.dyt, stream)
+    elif name == "gemm_dgrad":
+        mx_bf16_grouped_gemm_dgrad(dy, b.wt, b.off, E, cap, K, N, b.dx, od, stream)
+    elif name == "transpose_xt":
+        mx_bf16_gather(x, 1, T, K, b.src, cap, None, b.xt, stream)
+    elif name == "gemm_wgrad":
+        mx_bf16_grouped_gemm_wgrad(b.dyt, b.xt, b.off, E, cap, N, K, b.dw, od, stream)
+    else:
+        raise ValueError(name)
+
+
+def bf16_expert_step(b, x, w, dy, expert_ids, stream=None):
+    """One forward + backward pass of the BF16 baseline step."""
+    for name in BF16_STAGES:
+        run_bf16_stage(name, b, x, w, dy, expert_ids, stream)
+
+
+def bf16_work(T, K, N, E, topk, m_real=None):
+    """Bytes of the BF16 step's layout stages and of its GEMM operands (bf16
+    operands, bf16 outputs); the GEMM FLOPs are those of algorithmic_work."""
+    M = T * topk if m_real is None else m_real
+    cap = -(-(T * topk + 31 * E) // 32) * 32
+    return {
+        "gemm_operand_bytes": {"gemm_fwd": (M * K + E * N * K) * 2 + M * N * 2,
+                               "gemm_dgrad": (M * N + E * K * N) * 2 + M * K * 2,
+                               "gemm_wgrad": (N * M + K * M) * 2 + E * N * K * 2},
+        "bytes": {
+            "route": 4 * (T * topk * 2 + cap),
+            "permute_bf16": M * K * 2 + cap * K * 2 + 4 * cap,
+            "transpose_w": E * N * K * 4,
+            "transpose_dy": cap * N * 4,
+            "transpose_xt": M * K * 2 + cap * K * 2 + 4 * cap,
+        },
+    }
 
 
 def zero_pad_rows(dy_full, src_row):
