@@ -24,7 +24,11 @@ the fused rowwise+columnwise quantize and both dequantizes of a
 [16*8192, 5120] bf16 tensor.  ``swiglu_layer`` times the full SwiGLU expert
 FFN layer (64 experts, top-8, 32768 tokens, hidden 7168, ffn 2048) forward
 plus backward, stage by stage, including the router, SwiGLU and combine
-glue (and its fused-permute variant).  ``cpu_baseline`` times the oracle on a bounded sample (three
+glue (and its fused-permute variant).  ``bf16_baseline`` times the same
+expert step with bf16 operands (bf16 gather and transposes, bf16-MFMA grouped
+GEMMs of the same kernel design) and the MXFP8 speedup over it;
+``swiglu_layer.bf16_gemms`` does the same for the layer's six GEMMs.
+``cpu_baseline`` times the oracle on a bounded sample (three
 median-sized experts' share of the step).
 """
 
@@ -41,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_MXFP8_TFLOPS = 5000.0   # MI355X dense FP8/MXFP8 MFMA
 PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense BF16 MFMA
 METRIC = "MXFP8 grouped-GEMM TFLOP/s fwd+bwd and quantize GB/s, % of MI355X peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CALIB_BYTES = 1 << 30        # plain device copy used to scale the FETCH_SIZE / WRITE_SIZE counters
@@ -153,6 +158,7 @@ def gpu_expert_path(args, c):
              "stages": fused_stages,
              "note": "routing metadata + one gathered row+col quantize of the bf16 tokens replace quant_x, "
                      "the MXFP8 permute and quant_xt; bit-identical results"}
+    bf16 = gpu_bf16_step(args, c, x, w, dy, ids, work, step_ms, per)
     dom = max(work["gemm_flops"], key=lambda n: per[n])
     dom_tf = work["gemm_flops"][dom] / (per[dom] * 1e-3) / 1e12
     counts = np.bincount(c["expert_ids"].ravel(), minlength=E)
@@ -160,6 +166,7 @@ def gpu_expert_path(args, c):
     result = {
         "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
         "fused_quant_permute": fused,
+        "bf16_baseline": bf16,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4),
                      "traffic": None if tr is None else tr["bytes"],
@@ -174,6 +181,44 @@ def gpu_expert_path(args, c):
     del b, x, w, dy
     torch.cuda.empty_cache()
     return result
+
+
+def gpu_bf16_step(args, c, x, w, dy, ids, work, mx_step_ms, mx_per):
+    """The BF16 baseline of the same step on the same bf16 inputs: routing,
+    bf16 token gather, bf16 transposes in place of the columnwise quantizes,
+    and the three grouped GEMMs on bf16 operands (same kernel design, bf16
+    MFMA).  Reports its stages against the bf16 MFMA and HBM peaks and the
+    MXFP8 speedup over it (step and per GEMM)."""
+    import torch
+
+    from mxfp8_block_scaled_07_amd import MX_OUT_BF16, moe
+
+    T, K, N, E, topk = c["T"], c["K"], c["N"], c["E"], c["topk"]
+    b = moe.Bf16Buffers(T, K, N, E, topk, device="cuda:0", out_dtype=MX_OUT_BF16)
+    ms, per, _ = time_stages(lambda n: moe.run_bf16_stage(n, b, x, w, dy, ids), moe.BF16_STAGES, args.steps,
+                             args.warmup)
+    bw = moe.bf16_work(T, K, N, E, topk)
+    stages = {}
+    for n in moe.BF16_STAGES:
+        if n in work["gemm_flops"]:
+            tf = work["gemm_flops"][n] / (per[n] * 1e-3) / 1e12
+            stages[n] = {"ms": round(per[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "mxfp8_speedup": round(per[n] / mx_per[n], 3)}
+        else:
+            gbs = bw["bytes"][n] / (per[n] * 1e-3) / 1e9
+            stages[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+        tr = measured_traffic("bf16." + n)
+        stages[n]["traffic"] = None if tr is None else tr["bytes"]
+    gemm_ms = sum(per[n] for n in work["gemm_flops"])
+    mx_gemm_ms = sum(mx_per[n] for n in work["gemm_flops"])
+    flops = sum(work["gemm_flops"].values())
+    del b
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mxfp8_step_speedup": round(ms / mx_step_ms, 3), "mxfp8_gemm_speedup": round(gemm_ms / mx_gemm_ms, 3),
+            "peak_bf16_tflops": PEAK_BF16_TFLOPS, "stages": stages,
+            "note": "same step on bf16 operands: routing, bf16 token gather, bf16 transposes of W, dY and X_perm "
+                    "(the columnwise quantizes' counterparts), bf16-MFMA grouped GEMMs of the same kernel design"}
 
 
 def gpu_quantize_bandwidth(args):
@@ -262,9 +307,68 @@ def gpu_swiglu_layer(args):
         "stages": {n: {"ms": round(f_per[n], 4), "gbps": round(work["bytes"][n] / (f_per[n] * 1e-3) / 1e9, 1)}
                    for n in ("route", "quant_xperm")},
         "replaces": {n: round(per[n], 4) for n in ("quant_x", "permute", "quant_xt")}}
+    res["bf16_gemms"] = layer_bf16_gemms(args, b, x, w1, w2, per, work)
     del b, x, dout, w1, w2, logits
     torch.cuda.empty_cache()
     return res
+
+
+def layer_bf16_gemms(args, b, x, w1, w2, mx_per, work):
+    """The layer's six grouped GEMMs with bf16 operands (the BF16 baseline),
+    over the layer's own routing (group offsets of the MXFP8 run): operands
+    are the layer's bf16 tensors, gathered / transposed by mx_bf16_gather
+    (X_perm, W1^T, W2^T; the MXFP8 run's bf16 dA, dX_perm and H stand in for
+    A, dY and dH).  Each GEMM is timed like the MXFP8 stages and reported
+    with the MXFP8 speedup over it."""
+    import torch
+
+    import mxfp8_block_scaled_07_amd as mxa
+
+    T, H, F, E, cap = b.T, b.H, b.F, b.E, b.cap
+    dev, bf = x.device, torch.bfloat16
+    e = lambda *s: torch.empty(s, dtype=bf, device=dev)  # noqa: E731
+    xp, xt, w1t, w2t, at, dyt, dht = e(cap, H), e(H, cap), e(E, H, 2 * F), e(E, F, H), e(F, cap), e(H, cap), e(2 * F, cap)
+    mxa.mx_bf16_gather(x, 1, T, H, b.src, cap, xp, xt)
+    mxa.mx_bf16_gather(w1, E, 2 * F, H, None, 2 * F, None, w1t)
+    mxa.mx_bf16_gather(w2, E, H, F, None, H, None, w2t)
+    a, dy, dh = b.da, b.dxp, b.h
+    mxa.mx_bf16_gather(a, 1, cap, F, None, cap, None, at)
+    mxa.mx_bf16_gather(dy, 1, cap, H, None, cap, None, dyt)
+    mxa.mx_bf16_gather(dh, 1, cap, 2 * F, None, cap, None, dht)
+    o_h, o_y, o_da, o_dw2, o_dx, o_dw1 = e(cap, 2 * F), e(cap, H), e(cap, F), e(E, H, F), e(cap, H), e(E, 2 * F, H)
+    out = mxa.MX_OUT_BF16
+
+    def run(n):
+        if n == "gemm1_fwd":
+            mxa.mx_bf16_grouped_gemm_fwd(xp, w1, b.off, E, cap, 2 * F, H, o_h, out)
+        elif n == "gemm2_fwd":
+            mxa.mx_bf16_grouped_gemm_fwd(a, w2, b.off, E, cap, H, F, o_y, out)
+        elif n == "gemm2_dgrad":
+            mxa.mx_bf16_grouped_gemm_dgrad(dy, w2t, b.off, E, cap, F, H, o_da, out)
+        elif n == "gemm2_wgrad":
+            mxa.mx_bf16_grouped_gemm_wgrad(dyt, at, b.off, E, cap, H, F, o_dw2, out)
+        elif n == "gemm1_dgrad":
+            mxa.mx_bf16_grouped_gemm_dgrad(dh, w1t, b.off, E, cap, H, 2 * F, o_dx, out)
+        else:
+            mxa.mx_bf16_grouped_gemm_wgrad(dht, xt, b.off, E, cap, 2 * F, H, o_dw1, out)
+
+    names = ("gemm1_fwd", "gemm2_fwd", "gemm2_dgrad", "gemm2_wgrad", "gemm1_dgrad", "gemm1_wgrad")
+    torch.cuda.synchronize()
+    _, per, _ = time_stages(run, names, max(3, args.steps // 4), 2)
+    stages = {}
+    for n in names:
+        tf = work["gemm_flops"][n] / (per[n] * 1e-3) / 1e12
+        tr = measured_traffic("layer_bf16." + n)
+        stages[n] = {"ms": round(per[n], 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "mxfp8_speedup": round(per[n] / mx_per[n], 3), "traffic": None if tr is None else tr["bytes"]}
+    tot, mx_tot = sum(per[n] for n in names), sum(mx_per[n] for n in names)
+    del xp, xt, w1t, w2t, at, dyt, dht, o_h, o_y, o_da, o_dw2, o_dx, o_dw1
+    torch.cuda.empty_cache()
+    return {"ms": round(tot, 3), "mxfp8_ms": round(mx_tot, 3), "mxfp8_speedup": round(tot / mx_tot, 3),
+            "tflops": round(sum(work["gemm_flops"][n] for n in names) / (tot * 1e-3) / 1e12, 1),
+            "peak_bf16_tflops": PEAK_BF16_TFLOPS, "stages": stages,
+            "note": "the six grouped GEMMs of the layer on bf16 operands, same routing and kernel design; "
+                    "GEMMs only (the layer's glue kernels exist in their MXFP8-fused form only)"}
 
 
 def copy_calibration():
@@ -353,7 +457,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
         "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
-        "fused_quant_permute": res["fused_quant_permute"],
+        "fused_quant_permute": res["fused_quant_permute"], "bf16_baseline": res["bf16_baseline"],
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)
