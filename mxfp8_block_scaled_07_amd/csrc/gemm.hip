@@ -565,6 +565,9 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[4][4]) {
 // columns outside the tile get out-of-range offsets and are dropped, so
 // every wave issues exactly kTileStores store instructions per tile.
 constexpr int kEpiPitch = 272;
+// cache policy of the output stores: non-temporal (streamed; the output is
+// not read again by this kernel)
+constexpr int kStoreNt = 2;
 constexpr int kEpiSlice = 32 * kEpiPitch;
 static_assert(4 * kEpiSlice == kStageBytes, "the epilogue uses one LDS stage");
 
@@ -613,11 +616,11 @@ __device__ __forceinline__ void store_tile(const OutTile& o, const v16f (&acc)[4
         const uint32_t voff =
             (ml < o.rows) & (col < cols) ? (uint32_t)ml * (uint32_t)pitch + (uint32_t)(col * kEs) : kOob;
         if (kF32) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, a), r, voff, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, b), r, voff + 16, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, a), r, voff, 0, kStoreNt);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u_, b), r, voff + 16, 0, kStoreNt);
         } else {
           const v4u_ d = {bf16x2_rne(a.x, a.y), bf16x2_rne(a.z, a.w), bf16x2_rne(b.x, b.y), bf16x2_rne(b.z, b.w)};
-          __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, 0, kStoreNt);
         }
       }
       asm volatile("" ::: "memory");
