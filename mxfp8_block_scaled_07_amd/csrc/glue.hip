@@ -47,6 +47,7 @@ struct SrcSwiglu {
   int64_t F;
   struct Table {};
   static constexpr bool kTable = false;
+  static constexpr bool kGathered = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -87,6 +88,7 @@ struct SrcSwigluBwd {
   int64_t F;
   struct Table {};
   static constexpr bool kTable = false;
+  static constexpr bool kGathered = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -150,6 +152,7 @@ struct SrcCombineBwd {
     float w[kTq];
   };
   static constexpr bool kTable = true;
+  static constexpr bool kGathered = true;
   __device__ void fill_table(Table& tb, int64_t, int64_t r0, int64_t rows_out) const {
     const int t = threadIdx.x;
     if (t < kTq) {

@@ -25,6 +25,7 @@ struct SrcPlain {
   int64_t rows_in, cols;
   struct Table {};
   static constexpr bool kTable = false;
+  static constexpr bool kGathered = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -49,6 +50,7 @@ struct SrcGather {
     int32_t src[kTq];
   };
   static constexpr bool kTable = true;
+  static constexpr bool kGathered = true;
   __device__ void fill_table(Table& tb, int64_t, int64_t r0, int64_t rows_out) const {
     const int t = threadIdx.x;
     if (t < kTq) {

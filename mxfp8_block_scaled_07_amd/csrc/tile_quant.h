@@ -71,6 +71,7 @@ __device__ __forceinline__ uint32_t amax8(const uint4& v) {
 // Source concept:
 //   struct Table;                          LDS table filled once per tile (may be empty)
 //   static constexpr bool kTable;          whether fill_table must run
+//   static constexpr bool kGathered;       rows gathered from a source that other rows read again
 //   __device__ void fill_table(Table&, int64_t b, int64_t r0, int64_t rows_out) const;
 //   struct Row { bool ok; ... };
 //   __device__ Row row(const Table&, int64_t b, int64_t r, int local_r, bool in_range) const;
@@ -79,15 +80,31 @@ __device__ __forceinline__ uint32_t amax8(const uint4& v) {
 //   __device__ uint4 finish(const Raw&, const Row&, int64_t col) const;   8 bf16
 // Rows or columns outside the output, and rows the source marks !ok, are
 // zero: they raise no amax and produce zero codes (and zero pad scales).
+//
+// Tile order: consecutive blocks walk the column tiles of a row band (rows
+// stream through in order); for gathered sources, where each source row is
+// read again by other output rows (a token's k routed copies), they walk the
+// row bands of a column tile, so the re-reads of a source row's 256-byte
+// slice fall within the window of one column tile (all tokens x 256 B, a few
+// MB) and hit in the caches instead of HBM.
 template <class Src, bool kRow, bool kCol, bool kY>
 __global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const TqShape sh, const TqOut o) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kCol ? kTq * kTq * 2 : 16];
   __shared__ typename Src::Table table;
   uint32_t idx = blockIdx.x;
-  const int32_t tc = (int32_t)(idx % (uint32_t)sh.n_tc);
-  idx /= (uint32_t)sh.n_tc;
-  const int32_t tr = (int32_t)(idx % (uint32_t)sh.n_tr);
-  const int32_t b = (int32_t)(idx / (uint32_t)sh.n_tr);
+  int32_t tc, tr;
+  if (Src::kGathered) {
+    tr = (int32_t)(idx % (uint32_t)sh.n_tr);
+    idx /= (uint32_t)sh.n_tr;
+    tc = (int32_t)(idx % (uint32_t)sh.n_tc);
+    idx /= (uint32_t)sh.n_tc;
+  } else {
+    tc = (int32_t)(idx % (uint32_t)sh.n_tc);
+    idx /= (uint32_t)sh.n_tc;
+    tr = (int32_t)(idx % (uint32_t)sh.n_tr);
+    idx /= (uint32_t)sh.n_tr;
+  }
+  const int32_t b = (int32_t)idx;
   const int64_t r0 = (int64_t)tr * kTq, c0 = (int64_t)tc * kTq;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
