@@ -126,7 +126,9 @@ size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_t num_exper
  *   workspace     >= mx_permute_workspace_size(...) bytes of device memory
  * Rows of one expert keep the order of their flat pair index (stable), so
  * the result is deterministic.  Pad rows get codes 0x00 and scales 0x00.
- * Requires num_experts <= 16384 (MX_EUNSUPPORTED above).
+ * Each token's code row and scale bytes are read once and written to its
+ * topk rows.  Requires num_experts <= 16384 (MX_EUNSUPPORTED above); q and
+ * q_out 16-byte aligned, s and s_out 4-byte aligned.
  */
 int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
                int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,

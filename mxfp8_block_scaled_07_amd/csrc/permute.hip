@@ -14,7 +14,8 @@
 //   3. k_route_rank   one wave per tile walks its pairs in flat order; a pair's
 //                     row is its tile base + the number of earlier pairs of the
 //                     same expert (wave ballots give the in-chunk part)
-//   4. k_permute_rows copies q/s rows (pad rows -> zeros), 16 B per lane.
+//   4. k_permute_tokens copies each token's q/s row once to its topk rows,
+//                     16 B per lane, and zeroes the pad rows.
 
 #include "mx_device.h"
 
@@ -147,25 +148,61 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
 }
 
 // One wave per output row; 4 rows per block.  Rows copy codes then scales.
-__global__ void __launch_bounds__(256) k_permute_rows(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
-                                                      int64_t tokens, int64_t cols, const int32_t* __restrict__ src_row,
-                                                      int64_t capacity, uint8_t* __restrict__ q_out,
-                                                      uint8_t* __restrict__ s_out) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+// Token-major copy: block t < tokens reads token t's code row and scale
+// dwords once and writes them to its topk rows dst_row[t*topk + j] (ids out
+// of range have dst -1 and are skipped), so each source byte is read once
+// however many experts the token goes to.  Blocks past the tokens zero the
+// pad rows (src_row < 0), four rows per block.  Every output row is written
+// by exactly one block.
+__global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+                                                        int64_t tokens, int64_t cols, int32_t topk,
+                                                        const int32_t* __restrict__ dst_row,
+                                                        const int32_t* __restrict__ src_row, int64_t capacity,
+                                                        uint8_t* __restrict__ q_out, uint8_t* __restrict__ s_out) {
+  constexpr int kMaxK = 64;
+  __shared__ int32_t dl[kMaxK];
+  const int64_t nq = cols >> 4;          // 16-B chunks of codes (cols % 32 == 0)
+  const int64_t np = (cols + 127) >> 7;  // scale dwords: one per 128-column panel (panel-major)
+  const uint32_t* ss = reinterpret_cast<const uint32_t*>(s);
+  uint32_t* sd = reinterpret_cast<uint32_t*>(s_out);
+  const int64_t blk = blockIdx.x;
+  if (blk < tokens) {
+    const int64_t t = blk;
+    const uint4* qs = reinterpret_cast<const uint4*>(q + t * cols);
+    // slots in chunks of kMaxK (one chunk for every topk up to 64)
+    for (int32_t j0 = 0; j0 < topk; j0 += kMaxK) {
+      const int32_t nk = topk - j0 < kMaxK ? topk - j0 : kMaxK;
+      __syncthreads();  // the previous chunk's readers are done with dl
+      for (int j = threadIdx.x; j < nk; j += blockDim.x) {
+        const int32_t d = dst_row[t * topk + j0 + j];
+        dl[j] = d >= 0 && d < capacity ? d : -1;
+      }
+      __syncthreads();
+      for (int64_t i = threadIdx.x; i < nq; i += blockDim.x) {
+        const uint4 v = qs[i];
+        for (int j = 0; j < nk; ++j) {
+          const int32_t d = dl[j];
+          if (d >= 0) reinterpret_cast<uint4*>(q_out + (int64_t)d * cols)[i] = v;
+        }
+      }
+      for (int64_t p = threadIdx.x; p < np; p += blockDim.x) {
+        const uint32_t v = ss[p * tokens + t];
+        for (int j = 0; j < nk; ++j) {
+          const int32_t d = dl[j];
+          if (d >= 0) sd[p * capacity + d] = v;
+        }
+      }
+    }
+    return;
+  }
+  const int64_t r = (blk - tokens) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= capacity) return;
   const int32_t src = src_row[r];
-  const bool ok = src >= 0 && src < tokens;
-  const int64_t nq = cols >> 4;  // 16-B chunks of codes (cols % 32 == 0)
-  const uint4* qs = reinterpret_cast<const uint4*>(q + (ok ? src : 0) * cols);
+  if (src >= 0 && src < tokens) return;
   uint4* qd = reinterpret_cast<uint4*>(q_out + r * cols);
-  for (int64_t i = lane; i < nq; i += 64) qd[i] = ok ? qs[i] : make_uint4(0, 0, 0, 0);
-  // scales: one dword per 128-column panel (panel-major layout, pad bytes
-  // travel with their row)
-  const int64_t np = (cols + 127) >> 7;
-  const uint32_t* ss = reinterpret_cast<const uint32_t*>(s);
-  uint32_t* sd = reinterpret_cast<uint32_t*>(s_out);
-  for (int64_t p = lane; p < np; p += 64) sd[p * capacity + r] = ok ? ss[p * tokens + src] : 0u;
+  for (int64_t i = lane; i < nq; i += 64) qd[i] = make_uint4(0, 0, 0, 0);
+  for (int64_t p = lane; p < np; p += 64) sd[p * capacity + r] = 0u;
 }
 
 }  // namespace
@@ -194,6 +231,7 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (!group_offsets || !src_row || (tokens > 0 && (!expert_ids || !dst_row))) return MX_EINVAL;
   if (copy && (!q || !s || !q_out || !s_out || cols <= 0 || cols % 32)) return MX_EINVAL;
   if (copy && (((uintptr_t)s | (uintptr_t)s_out) & 3)) return MX_EINVAL;  // scale dwords
+  if (copy && (((uintptr_t)q | (uintptr_t)q_out) & 15)) return MX_EINVAL;  // 16-byte code copies
   const int64_t n = tokens * topk;
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
   if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;
@@ -217,8 +255,11 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (n > 0)
     hipLaunchKernelGGL(k_route_rank, dim3((unsigned)nt), dim3(64), lds, st, expert_ids, n, topk, num_experts, tile,
                        base, dst_row, src_row, capacity_rows);
-  if (copy && capacity_rows > 0)
-    hipLaunchKernelGGL(k_permute_rows, dim3((unsigned)((capacity_rows + 3) / 4)), dim3(256), 0, st, q, s, tokens,
-                       cols, src_row, capacity_rows, q_out, s_out);
+  if (copy && capacity_rows > 0) {
+    const int64_t blocks = tokens + (capacity_rows + 3) / 4;
+    if (blocks > 0x7FFFFFFF) return MX_EINVAL;
+    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)blocks), dim3(256), 0, st, q, s, tokens, cols, topk, dst_row,
+                       src_row, capacity_rows, q_out, s_out);
+  }
   return launch_status();
 }

@@ -87,3 +87,29 @@ def test_permute_deterministic():
     a = check_permute(c["expert_ids"], 16, K=128)
     b = check_permute(c["expert_ids"], 16, K=128)
     assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("T,topk,E", [(200, 70, 80), (40, 129, 5)])
+def test_topk_above_64(T, topk, E):
+    """More routed copies per token than the permute's 64-slot table holds:
+    the slots are copied in chunks of 64."""
+    g = np.random.default_rng(T + topk)
+    check_permute(g.integers(0, E, (T, topk)), E, K=96, seed=topk)
+
+
+def test_permute_rejects_misaligned_codes():
+    T, K, E, topk = 64, 64, 2, 2
+    ids = torch.zeros((T, topk), dtype=torch.int32, device="cuda:0")
+    cap = T * topk + 31 * E
+    buf = torch.zeros(T * K + 16, dtype=torch.uint8, device="cuda:0")
+    q = buf[8:8 + T * K]                                  # 8-byte aligned only
+    s = torch.zeros(mxa.scale_shape(T, K), dtype=torch.uint8, device="cuda:0")
+    q_out = torch.zeros((cap, K), dtype=torch.uint8, device="cuda:0")
+    s_out = torch.zeros(mxa.scale_shape(cap, K), dtype=torch.uint8, device="cuda:0")
+    off = torch.zeros(E + 1, dtype=torch.int32, device="cuda:0")
+    dst = torch.zeros(T * topk, dtype=torch.int32, device="cuda:0")
+    src = torch.zeros(cap, dtype=torch.int32, device="cuda:0")
+    wsb = mxa.mx_permute_workspace_size(T, topk, E)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(mxa.MXError):
+        mxa.mx_permute(q, s, T, K, ids, topk, E, cap, q_out, s_out, off, dst, src, ws, wsb)
