@@ -89,8 +89,14 @@ __device__ __forceinline__ uint32_t amax8(const uint4& v) {
 // MB) and hit in the caches instead of HBM.
 template <class Src, bool kRow, bool kCol, bool kY>
 __global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const TqShape sh, const TqOut o) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kCol ? kTq * kTq * 2 : 16];
-  __shared__ typename Src::Table table;
+  // The source's row table is only read while the tile is loaded, before the
+  // column phase writes the LDS tile: it shares the tile's first bytes, so a
+  // gathered tile needs no more LDS than a plain one (5 workgroups per CU).
+  typedef typename Src::Table Table;
+  constexpr int kTile = kCol ? kTq * kTq * 2 : 16;
+  constexpr int kLds = kTile > (int)sizeof(Table) ? kTile : (int)sizeof(Table);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
+  Table& table = *reinterpret_cast<Table*>(lds);
   uint32_t idx = blockIdx.x;
   int32_t tc, tr;
   if (Src::kGathered) {
@@ -154,6 +160,7 @@ __global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const 
   }
 
   if (kCol) {
+    if (Src::kTable) __syncthreads();  // every wave is done with the row table (it shares the LDS tile)
     const int slot = lr0 >> 3;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
