@@ -32,7 +32,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"mx_quantize", "mx_dequantize", "mx_permute", "mx_permute_workspace_size",
                           "mx_grouped_gemm_fwd", "mx_grouped_gemm_dgrad", "mx_grouped_gemm_wgrad",
                           "mx_status_string", "mx_swiglu_quantize", "mx_swiglu_bwd_quantize", "mx_combine",
-                          "mx_combine_bwd_quantize", "mx_route_topk", "mx_router_bwd"}
+                          "mx_combine_bwd_quantize", "mx_route_topk", "mx_router_bwd", "mx_bf16_gather",
+                          "mx_bf16_grouped_gemm_fwd", "mx_bf16_grouped_gemm_dgrad", "mx_bf16_grouped_gemm_wgrad"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +104,38 @@ def test_quantize_alignment(lib):
     assert q(Q, 1, 32, 32, None, 32, P, P, None, None, None) == mxa.MX_EINVAL             # x not 16-aligned
     assert q(P, 1, 32, 32, None, 32, None, None, Q, P, None) == mxa.MX_EINVAL             # col codes
     assert q(P, 1, 32, 32, None, 32, P, ctypes.c_void_p(18), None, None, None) == mxa.MX_EINVAL   # scales
+
+
+def test_permute_code_alignment(lib):
+    ws = lib.mx_permute_workspace_size(100, 2, 4)
+    p = lib.mx_permute
+    assert p(Q, P, 100, 64, P, 2, 4, 400, P, P, P, P, P, P, ws, None) == mxa.MX_EINVAL   # codes not 16-aligned
+    assert p(P, P, 100, 64, P, 2, 4, 400, Q, P, P, P, P, P, ws, None) == mxa.MX_EINVAL
+
+
+def test_bf16_validation(lib):
+    g = lib.mx_bf16_gather
+    assert g(None, 1, 64, 64, None, 64, P, None, None) == mxa.MX_EINVAL        # x null
+    assert g(P, 1, 64, 64, None, 64, None, None, None) == mxa.MX_EINVAL        # no output
+    assert g(P, 1, 64, 48, None, 64, P, None, None) == mxa.MX_EINVAL           # cols % 32
+    assert g(P, 1, 64, 64, None, 48, P, None, None) == mxa.MX_EINVAL           # rows_out % 32
+    assert g(P, 1, 64, 64, None, 32, P, None, None) == mxa.MX_EINVAL           # rows_out < rows, no gather
+    assert g(P, 2, 64, 64, P, 64, P, None, None) == mxa.MX_EINVAL              # gather with batch > 1
+    assert g(Q, 1, 64, 64, None, 64, P, None, None) == mxa.MX_EINVAL           # x not 16-aligned
+    assert g(P, 1, 0, 64, None, 0, P, None, None) == mxa.MX_OK                 # no rows: nothing to do
+    for fn in (lib.mx_bf16_grouped_gemm_fwd, lib.mx_bf16_grouped_gemm_dgrad):
+        assert fn(P, P, P, 2, 64, 48, 64, P, 0, None) == mxa.MX_EINVAL          # n % 32
+        assert fn(P, P, P, 2, 64, 64, 40, P, 0, None) == mxa.MX_EINVAL          # k % 32
+        assert fn(P, P, P, 0, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL          # no groups
+        assert fn(P, P, P, 2, 64, 64, 64, P, 7, None) == mxa.MX_EINVAL          # dtype
+        assert fn(Q, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL          # a not 16-aligned
+        assert fn(P, P, None, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL       # offsets null
+        assert fn(P, P, P, 2, 0, 64, 64, P, 0, None) == mxa.MX_OK               # no rows
+        assert fn(P, P, P, 5000, 64, 64, 64, P, 0, None) == mxa.MX_EUNSUPPORTED  # too many groups
+    w = lib.mx_bf16_grouped_gemm_wgrad
+    assert w(P, P, P, 2, 48, 64, 64, P, 0, None) == mxa.MX_EINVAL              # m_cap % 32
+    assert w(P, Q, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL              # xt not 16-aligned
+    assert w(P, P, P, 5000, 64, 64, 64, P, 0, None) == mxa.MX_EUNSUPPORTED
 
 
 def test_swiglu_validation(lib):
