@@ -28,6 +28,8 @@ glue (and its fused-permute variant).  ``bf16_baseline`` times the same
 expert step with bf16 operands (bf16 gather and transposes, bf16-MFMA grouped
 GEMMs of the same kernel design) and the MXFP8 speedup over it;
 ``swiglu_layer.bf16_gemms`` does the same for the layer's six GEMMs.
+``graph`` (and ``swiglu_layer.graph``) replays the step captured once in a
+HIP graph.
 ``cpu_baseline`` times the oracle on a bounded sample (three
 median-sized experts' share of the step).
 """
@@ -108,6 +110,23 @@ def time_stages(run, names, steps, warmup):
     return total_ms / steps, per, wall
 
 
+def time_graph(g, steps, warmup):
+    """ms per replay of a captured step: ``warmup`` untimed replays, then
+    ``steps`` replays between two events on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def gpu_expert_path(args, c):
     import numpy as np
     import torch
@@ -158,6 +177,13 @@ def gpu_expert_path(args, c):
              "stages": fused_stages,
              "note": "routing metadata + one gathered row+col quantize of the bf16 tokens replace quant_x, "
                      "the MXFP8 permute and quant_xt; bit-identical results"}
+    # the same step captured once in a HIP graph and replayed (no host launch
+    # gaps, no per-stage events)
+    graph = moe.capture(lambda: moe.expert_step(b, x, w, dy, ids))
+    g_ms = time_graph(graph, args.steps, args.warmup)
+    del graph
+    graph_res = {"ms_per_step": round(g_ms, 4), "tflops": round(sum(work["gemm_flops"].values()) / (g_ms * 1e-3) / 1e12, 1),
+                 "note": "the step's launches captured in one HIP graph (torch.cuda.CUDAGraph) and replayed"}
     bf16 = gpu_bf16_step(args, c, x, w, dy, ids, work, step_ms, per)
     dom = max(work["gemm_flops"], key=lambda n: per[n])
     dom_tf = work["gemm_flops"][dom] / (per[dom] * 1e-3) / 1e12
@@ -166,6 +192,7 @@ def gpu_expert_path(args, c):
     result = {
         "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
         "fused_quant_permute": fused,
+        "graph": graph_res,
         "bf16_baseline": bf16,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4),
@@ -307,6 +334,10 @@ def gpu_swiglu_layer(args):
         "stages": {n: {"ms": round(f_per[n], 4), "gbps": round(work["bytes"][n] / (f_per[n] * 1e-3) / 1e9, 1)}
                    for n in ("route", "quant_xperm")},
         "replaces": {n: round(per[n], 4) for n in ("quant_x", "permute", "quant_xt")}}
+    graph = moe.capture(lambda: moe.layer_step(b, x, w1, w2, logits, dout))
+    g_ms = time_graph(graph, steps, 2)
+    del graph
+    res["graph"] = {"ms_per_step": round(g_ms, 3), "tflops": round(flops / (g_ms * 1e-3) / 1e12, 1)}
     res["bf16_gemms"] = layer_bf16_gemms(args, b, x, w1, w2, per, work)
     del b, x, dout, w1, w2, logits
     torch.cuda.empty_cache()
@@ -457,7 +488,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
         "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
-        "fused_quant_permute": res["fused_quant_permute"], "bf16_baseline": res["bf16_baseline"],
+        "fused_quant_permute": res["fused_quant_permute"], "graph": res["graph"],
+        "bf16_baseline": res["bf16_baseline"],
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)

@@ -185,6 +185,25 @@ def bf16_work(T, K, N, E, topk, m_real=None):
     }
 
 
+def capture(fn, warm=2):
+    """Capture one call of ``fn`` -- a step whose calls launch on torch's
+    current stream and allocate nothing -- into a HIP graph
+    (torch.cuda.CUDAGraph); ``graph.replay()`` then relaunches the whole step
+    without host launch overhead.  ``fn`` runs ``warm`` times on a side
+    stream first.  The library's kernels write every output they own on each
+    call, so a replay reproduces the eager step bit for bit."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(warm):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 def zero_pad_rows(dy_full, src_row):
     """dY in the padded permuted layout: rows whose src_row is -1 (pad rows
     and rows past the last group) set to zero (test/bench input preparation)."""
