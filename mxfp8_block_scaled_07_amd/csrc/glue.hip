@@ -16,7 +16,9 @@
 //   dY[dst_row[i]] = w[i] dOut[i / k]          (one fp32 product)
 // sigmoid uses e = exp(-|g|) in (0, 1]: sigmoid(|g|) = 1 / (1 + e) and
 // sigmoid(-|g|) = e / (1 + e), so neither 1 - sigmoid nor a large exponent
-// is ever formed.
+// is ever formed.  1 + e lies in (1, 2], so its reciprocal is the hardware
+// one (V_RCP_F32, within 1 ulp; no denormal can occur) instead of a
+// correctly rounded division sequence.
 
 #include "tile_quant.h"
 
@@ -29,7 +31,7 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // silu(g) and the two sigmoids sigmoid(g), sigmoid(-g).
 __device__ __forceinline__ float silu_parts(float g, float& s, float& sm) {
   const float e = expf(-fabsf(g));
-  const float r = 1.0f / (1.0f + e);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
   const float er = e * r;
   s = g >= 0.0f ? r : er;
   sm = g >= 0.0f ? er : r;
@@ -106,10 +108,11 @@ struct SrcSwigluBwd {
     uint4 g, u, d;
   };
   __device__ Raw fetch(const Row& w, int64_t col) const {
-    const int64_t c = col < F ? col : col - F;
+    const bool gate = col < F;  // du needs no u
+    const int64_t c = gate ? col : col - F;
     Raw x;
     x.g = *reinterpret_cast<const uint4*>(w.ph + c);
-    x.u = *reinterpret_cast<const uint4*>(w.ph + F + c);
+    x.u = gate ? *reinterpret_cast<const uint4*>(w.ph + F + c) : make_uint4(0, 0, 0, 0);
     x.d = *reinterpret_cast<const uint4*>(w.pd + c);
     return x;
   }
