@@ -225,3 +225,26 @@ def test_bf16_step_full_size(out_dtype):
         D, X = f64(dy_np[lo:hi][:, ns]), f64(xp[lo:hi][:, ks])
         res = tolerance.check(dw[e][np.ix_(ns, ks)], D.T @ X, np.abs(D).T @ np.abs(X), out_bf16=True)
         assert res["ok"], ("wgrad", e, res)
+
+
+def test_gather_all_pad_rows():
+    x = np.arange(64 * 32, dtype=np.uint16).reshape(64, 32)
+    o_rows, o_cols = gpu_gather(x, 1, 64, 32, np.full(96, -1), 96)
+    assert not o_rows.any() and not o_cols.any()
+
+
+def test_max_groups_fwd_and_wgrad():
+    """2048 groups, the most one call takes, most of them tiny or empty:
+    forward over ragged groups of 0 to 64 rows, wgrad over groups of 0, 32
+    or 64 rows; both compared in full."""
+    g = np.random.default_rng(4096)
+    E, N, K = 2048, 64, 96
+    sizes = g.choice([0, 0, 1, 17, 32, 45, 64], E)
+    counts, off, dst, src = routing.route(workloads.ids_from_sizes(sizes), E)
+    a = ob.gather(workloads.normal_bf16(g, (int(sizes.sum()), K), 1.0, 0.01), src, len(src))
+    b = workloads.normal_bf16(g, (E, N, K), 0.02, 0.0)
+    check_rows("fwd", a, b, off, mxa.MX_OUT_F32)
+    woff = np.concatenate([[0], np.cumsum(g.choice([0, 32, 64], E))])
+    cap = int(woff[-1]) + 32
+    check_wgrad(workloads.normal_bf16(g, (N, cap), 1.0, 0.0), workloads.normal_bf16(g, (K, cap), 1.0, 0.0),
+                woff, mxa.MX_OUT_F32)
