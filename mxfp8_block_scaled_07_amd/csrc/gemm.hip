@@ -883,6 +883,8 @@ static int gemm_rows(const uint8_t* a_q, const uint8_t* a_s, const uint8_t* b_q,
                      int32_t out_dtype, mx_stream_t stream) {
   if (!a_q || !a_s || !b_q || !b_s || !offsets || !out) return MX_EINVAL;
   if (((uintptr_t)a_s | (uintptr_t)b_s) & 3) return MX_EINVAL;  // scale dwords
+  // 16-byte LDS-direct operand loads and 16-byte output stores
+  if (((uintptr_t)a_q | (uintptr_t)b_q | (uintptr_t)out) & 15) return MX_EINVAL;
   if (E < 1 || m_cap < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * K >= (1ll << 31) || m_cap >= (1ll << 31)) return MX_EINVAL;  // 32-bit tile spans and bounds
@@ -916,6 +918,8 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
                                      mx_stream_t stream) {
   if (!dyt_q || !dyt_s || !xt_q || !xt_s || !group_offsets || !dw) return MX_EINVAL;
   if (((uintptr_t)dyt_s | (uintptr_t)xt_s) & 3) return MX_EINVAL;  // scale dwords
+  // 16-byte LDS-direct operand loads and 16-byte output stores
+  if (((uintptr_t)dyt_q | (uintptr_t)xt_q | (uintptr_t)dw) & 15) return MX_EINVAL;
   if (num_groups < 1 || m_cap < 0 || m_cap % 32 || n <= 0 || k <= 0 || n % 32 || k % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * m_cap >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile
@@ -936,7 +940,7 @@ extern "C" int mx_grouped_gemm_wgrad(const uint8_t* dyt_q, const uint8_t* dyt_s,
 static int bf16_rows(const uint16_t* a, const uint16_t* b, const int32_t* offsets, int32_t E, int64_t m_cap,
                      int64_t N, int64_t K, void* out, int32_t out_dtype, mx_stream_t stream) {
   if (!a || !b || !offsets || !out) return MX_EINVAL;
-  if (((uintptr_t)a | (uintptr_t)b) & 15) return MX_EINVAL;  // 16-byte operand loads
+  if (((uintptr_t)a | (uintptr_t)b | (uintptr_t)out) & 15) return MX_EINVAL;  // 16-byte operand loads and stores
   if (E < 1 || m_cap < 0 || N <= 0 || K <= 0 || N % 32 || K % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * 2 * K >= (1ll << 31) || m_cap >= (1ll << 31)) return MX_EINVAL;  // 32-bit tile spans and bounds
@@ -966,7 +970,7 @@ extern "C" int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* x
                                           int32_t num_groups, int64_t m_cap, int64_t n, int64_t k, void* dw,
                                           int32_t out_dtype, mx_stream_t stream) {
   if (!dyt || !xt || !group_offsets || !dw) return MX_EINVAL;
-  if (((uintptr_t)dyt | (uintptr_t)xt) & 15) return MX_EINVAL;  // 16-byte operand loads
+  if (((uintptr_t)dyt | (uintptr_t)xt | (uintptr_t)dw) & 15) return MX_EINVAL;  // 16-byte operand loads and stores
   if (num_groups < 1 || m_cap < 0 || m_cap % 32 || n <= 0 || k <= 0 || n % 32 || k % 32) return MX_EINVAL;
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return MX_EINVAL;
   if ((int64_t)BM * 2 * m_cap >= (1ll << 31)) return MX_EINVAL;  // buffer-resource span of one tile

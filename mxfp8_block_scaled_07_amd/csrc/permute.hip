@@ -239,6 +239,8 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   const int32_t tile = route_tile(num_experts);
   const int64_t nt = route_tiles(n, num_experts) > 0 ? route_tiles(n, num_experts) : 1;
   if (nt > 0x7FFFFFFF) return MX_EINVAL;
+  const int64_t copy_blocks = tokens + (capacity_rows + 3) / 4;  // k_permute_tokens grid
+  if (copy && copy_blocks > 0x7FFFFFFF) return MX_EINVAL;
   int32_t* hist = static_cast<int32_t*>(workspace);
   int32_t* base = hist + nt * num_experts;
   const size_t lds = (size_t)num_experts * sizeof(int32_t);  // <= 64 KB (kMaxExperts)
@@ -255,11 +257,8 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (n > 0)
     hipLaunchKernelGGL(k_route_rank, dim3((unsigned)nt), dim3(64), lds, st, expert_ids, n, topk, num_experts, tile,
                        base, dst_row, src_row, capacity_rows);
-  if (copy && capacity_rows > 0) {
-    const int64_t blocks = tokens + (capacity_rows + 3) / 4;
-    if (blocks > 0x7FFFFFFF) return MX_EINVAL;
-    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)blocks), dim3(256), 0, st, q, s, tokens, cols, topk, dst_row,
-                       src_row, capacity_rows, q_out, s_out);
-  }
+  if (copy && capacity_rows > 0)
+    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)copy_blocks), dim3(256), 0, st, q, s, tokens, cols, topk,
+                       dst_row, src_row, capacity_rows, q_out, s_out);
   return launch_status();
 }

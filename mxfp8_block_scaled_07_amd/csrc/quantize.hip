@@ -142,6 +142,8 @@ extern "C" int mx_quantize(const uint16_t* x, int64_t batch, int64_t rows, int64
 extern "C" int mx_dequantize(const uint8_t* q, const uint8_t* s, int64_t rows, int64_t cols, uint16_t* y,
                              mx_stream_t stream) {
   if (!q || !s || !y || rows < 0 || cols <= 0 || cols % 32) return MX_EINVAL;
+  // 16 codes in and 16 bf16 out per thread (16-byte accesses); scale dwords
+  if ((((uintptr_t)q | (uintptr_t)y) & 15) || ((uintptr_t)s & 3)) return MX_EINVAL;
   if (rows == 0) return MX_OK;
   const int64_t blocks = (rows * (cols / 16) + 255) / 256;
   if (blocks > 0x7FFFFFFF) return MX_EINVAL;

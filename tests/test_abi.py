@@ -106,6 +106,38 @@ def test_quantize_alignment(lib):
     assert q(P, 1, 32, 32, None, 32, P, ctypes.c_void_p(18), None, None, None) == mxa.MX_EINVAL   # scales
 
 
+def test_gemm_alignment(lib):
+    """Codes feed 16-byte LDS-direct loads and outputs take 16-byte stores:
+    misaligned code or output pointers are rejected (scales need 4 bytes)."""
+    for fn in (lib.mx_grouped_gemm_fwd, lib.mx_grouped_gemm_dgrad, lib.mx_grouped_gemm_wgrad):
+        assert fn(Q, P, P, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL      # a codes
+        assert fn(P, P, Q, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL      # b codes
+        assert fn(P, P, P, P, P, 2, 64, 64, 64, Q, 0, None) == mxa.MX_EINVAL      # output
+        assert fn(P, ctypes.c_void_p(18), P, P, P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL   # a scales
+        assert fn(P, P, P, ctypes.c_void_p(18), P, 2, 64, 64, 64, P, 0, None) == mxa.MX_EINVAL   # b scales
+    for fn in (lib.mx_bf16_grouped_gemm_fwd, lib.mx_bf16_grouped_gemm_dgrad, lib.mx_bf16_grouped_gemm_wgrad):
+        assert fn(P, P, P, 2, 64, 64, 64, Q, 0, None) == mxa.MX_EINVAL            # output
+
+
+def test_dequantize_alignment(lib):
+    d = lib.mx_dequantize
+    assert d(Q, P, 4, 32, P, None) == mxa.MX_EINVAL                                # codes
+    assert d(P, P, 4, 32, Q, None) == mxa.MX_EINVAL                                # bf16 output
+    assert d(P, ctypes.c_void_p(18), 4, 32, P, None) == mxa.MX_EINVAL              # scales
+
+
+def test_permute_grid_limit_checked_before_any_launch(lib):
+    """A copy grid beyond 2^31 - 1 blocks is rejected up front (before the
+    routing kernels are enqueued); on a machine without a GPU any launch
+    would return MX_EHIP instead."""
+    tokens = (1 << 31) - 100
+    cap = tokens + 31
+    ws = lib.mx_permute_workspace_size(tokens, 1, 1)
+    assert ws > 0
+    p = lib.mx_permute
+    assert p(P, P, tokens, 32, P, 1, 1, cap, P, P, P, P, P, P, ws, None) == mxa.MX_EINVAL
+
+
 def test_permute_code_alignment(lib):
     ws = lib.mx_permute_workspace_size(100, 2, 4)
     p = lib.mx_permute

@@ -13,7 +13,7 @@ from oracle import gemm as og
 from oracle import mxfp8 as mx
 from oracle import routing, tolerance
 
-from gpu_util import dev, host, rows_h_fn, spanels, wgrad_h_fn
+from gpu_util import MAX_ERR_OVER_S, dev, host, model_check_rows, model_check_wgrad, rows_h_fn, spanels, wgrad_h_fn
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,11 @@ def check_rows(kind, a_q, a_s, b_q, b_s, off, out_dtype):
         a_q, a_s, b_q, b_s, off, N)(i + lo * N), out_bf16=out_dtype == mxa.MX_OUT_BF16)
     print(kind, res)
     assert res["ok"], res
+    assert res["max_err_over_S"] <= MAX_ERR_OVER_S, res
+    rm = model_check_rows(got, a_q, a_s, b_q, b_s, off, N, np.random.default_rng(N + K),
+                          out_bf16=out_dtype == mxa.MX_OUT_BF16)
+    print(kind, "model", rm)
+    assert rm is None or rm["ok"], rm
     # rows outside every group are left untouched
     outside = np.r_[0:lo, hi:a_q.shape[0]]
     if outside.size:
@@ -101,6 +106,11 @@ def check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, out_dtype):
                           out_bf16=out_dtype == mxa.MX_OUT_BF16)
     print("wgrad", res)
     assert res["ok"], res
+    assert res["max_err_over_S"] <= MAX_ERR_OVER_S, res
+    rm = model_check_wgrad(got, dyt_q, dyt_s, xt_q, xt_s, off, np.random.default_rng(N + K),
+                           out_bf16=out_dtype == mxa.MX_OUT_BF16)
+    print("wgrad model", rm)
+    assert rm is None or rm["ok"], rm
     for e in range(E):
         if off[e + 1] == off[e]:
             z = got[e].astype(np.float64) if out_dtype == mxa.MX_OUT_F32 else got[e]

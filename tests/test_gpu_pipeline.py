@@ -163,3 +163,93 @@ def test_fused_quantize_permute_matches_full_path(case):
     for name in ("y", "dx"):
         assert torch.equal(getattr(a, name)[:hi].view(torch.int16), getattr(f, name)[:hi].view(torch.int16)), name
     assert torch.equal(a.dw.view(torch.int16), f.dw.view(torch.int16))
+
+
+def grade_tile(name, got, aq, as_, bq, bs, is_bf16, g):
+    """Every element of an output tile got [R, Cc] against the exact products
+    of operand rows aq [R, L] and bq [Cc, L] (scales [., L/32]); rows are
+    aligned so that index 0 starts a k step of the kernel.  Pass rule with H,
+    the err/S ceiling, and the instruction-model check on 4096 samples."""
+    from gpu_util import MAX_ERR_OVER_S
+    A, B = mx.mx_values(aq, as_), mx.mx_values(bq, bs)
+    C, S = A @ B.T, np.abs(A) @ np.abs(B).T
+    EA, EB = tolerance.nominal_exponents(aq, as_), tolerance.nominal_exponents(bq, bs)
+    Cc = bq.shape[0]
+
+    def h_fn(idx):
+        out = np.zeros(idx.size)
+        for c0 in range(0, idx.size, 2048):
+            i, j = np.divmod(idx[c0:c0 + 2048], Cc)
+            out[c0:c0 + 2048] = tolerance.hardware_term(EA[i], EB[j])
+        return out
+
+    res = tolerance.check(got.ravel(), C.ravel(), S.ravel(), h_fn=h_fn, out_bf16=is_bf16)
+    print(name, got.shape, res)
+    assert res["ok"], (name, res)
+    assert res["max_err_over_S"] <= MAX_ERR_OVER_S, (name, res)
+    i = g.integers(0, got.shape[0], 4096)
+    j = g.integers(0, Cc, 4096)
+    model, bound = tolerance.mfma_model(aq[i], as_[i], bq[j], bs[j])
+    rm = tolerance.check_model(got[i, j], model, bound, out_bf16=is_bf16)
+    print(name, "model", rm)
+    assert rm["ok"], (name, rm)
+    return res
+
+
+def test_expert_step_whole_tiles(case):
+    """Whole output tiles of the large workload's GEMMs, as the benchmark runs
+    them (bf16 outputs), against the oracle on the kernel's own MX operand
+    bytes: for fwd and dgrad the last, partly filled 256-row tile of three
+    groups (the smallest, the largest, and one next to the empty expert) over
+    the first and last 256 output columns; for wgrad a full 256 x 256 dW tile
+    of three groups whose rows start inside a 128-row scale panel."""
+    c, x, w, ids, dy, dy_np, (counts, off, dst, src) = case
+    T, K, N, E, topk, cap = c["T"], c["K"], c["N"], c["E"], c["topk"], c["capacity"]
+    b = moe.ExpertBuffers(T, K, N, E, topk, out_dtype=MX_OUT_BF16)
+    moe.expert_step(b, x, w, dy, ids)
+    torch.cuda.synchronize()
+    g = np.random.default_rng(77)
+    live = [e for e in range(E) if counts[e] > 0]
+    empty = [e for e in range(E) if counts[e] == 0]
+    nxt = [e for e in live if abs(e - empty[0]) == 1]
+    groups = sorted({min(live, key=lambda e: counts[e]), max(live, key=lambda e: counts[e]), nxt[0]})
+    xpq, xps = host(b.xpq), srows(b.xps, K)
+    dyq, dys = host(b.dyq), srows(b.dys, N)
+    wq, ws = host(b.wq), srows(b.wsc, K)
+    wtq, wts = host(b.wtq), srows(b.wtsc, N)
+    y, dx, dw = host(b.y), host(b.dx), host(b.dw)
+    for e in groups:
+        lo, hi = int(off[e]), int(off[e + 1])
+        r0 = lo + 256 * ((hi - lo - 1) // 256)             # the group's last m tile
+        rows = np.arange(r0, hi)
+        # the kernel's operand bytes are the oracle's quantize of the inputs
+        oq, os_ = mx.quantize_rowwise(mx.gather_rows(c["x"], src[rows], rows.size))
+        assert np.array_equal(xpq[rows], oq) and np.array_equal(xps[rows], os_)
+        oq, os_ = mx.quantize_rowwise(dy_np[rows])
+        assert np.array_equal(dyq[rows], oq) and np.array_equal(dys[rows], os_)
+        for cols in (np.arange(0, 256), np.arange(N - 256, N)):
+            grade_tile(f"fwd e={e} rows {r0}:{hi} cols {cols[0]}", y[np.ix_(rows, cols)], xpq[rows], xps[rows],
+                       wq[e][cols], ws[e * N + cols], True, g)
+        for cols in (np.arange(0, 256), np.arange(K - 256, K)):
+            grade_tile(f"dgrad e={e} rows {r0}:{hi} cols {cols[0]}", dx[np.ix_(rows, cols)], dyq[rows], dys[rows],
+                       wtq[e][cols], wts[e * K + cols], True, g)
+    # wgrad: groups whose rows start inside a 128-row panel
+    dytq, dyts = host(b.dytq), srows(b.dyts, cap)
+    xtq, xts = host(b.xtq), srows(b.xts, cap)
+    mid = [e for e in live if off[e] % 128 != 0]
+    assert len(mid) >= 3
+    for e in mid[:3]:
+        lo, hi = int(off[e]), int(off[e + 1])
+        kb = lo & ~127
+        n0 = 256 * int(g.integers(0, N // 256))
+        k0 = 256 * int(g.integers(0, K // 256))
+        nr, kr = np.arange(n0, n0 + 256), np.arange(k0, k0 + 256)
+        aq = dytq[nr, kb:hi].copy()
+        bq = xtq[kr, kb:hi].copy()
+        aq[:, :lo - kb] = 0
+        bq[:, :lo - kb] = 0
+        # the kernel's columnwise bytes of this group are the oracle's
+        cq, cs = mx.quantize_rowwise(np.ascontiguousarray(dy_np[lo:hi, n0:n0 + 256].T))
+        assert np.array_equal(dytq[nr, lo:hi], cq) and np.array_equal(dyts[nr, lo // 32:hi // 32], cs)
+        grade_tile(f"wgrad e={e} rows {lo}:{hi} tile ({n0},{k0})", dw[e][np.ix_(nr, kr)], aq,
+                   dyts[nr, kb // 32:hi // 32], bq, xts[kr, kb // 32:hi // 32], True, g)
