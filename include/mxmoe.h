@@ -136,6 +136,26 @@ int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols,
                size_t workspace_bytes, mx_stream_t stream);
 
 /*
+ * mx_permute for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results and checks without `workspace`.  The routing
+ * tables live in a library-owned device array of
+ * MX_PERMUTE_NOALLOC_SCRATCH_BYTES bytes, one per GPU, held until the
+ * process ends; its address is looked up on the first call on each device
+ * (hipGetSymbolAddress, no allocation).  Requests whose
+ * mx_permute_workspace_size exceeds it return MX_EUNSUPPORTED (use
+ * mx_permute then).  All calls on one GPU share that array: calls that
+ * overlap in time on one GPU (different streams, or threads without
+ * ordering) race and must not be issued; calls on one stream are ordered
+ * and safe.  Nothing is carried from one call to the next (every table entry
+ * is written before it is read).
+ */
+#define MX_PERMUTE_NOALLOC_SCRATCH_BYTES (4u << 20)
+int mx_permute_noalloc(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
+                       int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,
+                       int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, mx_stream_t stream);
+
+/*
  * Block-scaled grouped GEMMs (digest "Key Questions Answered": block-scaled
  * MMA; PR #3203 "Next steps": grouped GEMM on pre-quantized tensors).  All
  * three are C[m, n] = sum_k A[m, k] B[n, k] with both operands contiguous

@@ -28,6 +28,7 @@ _SIGNATURES = {
     "mx_dequantize": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "mx_permute_workspace_size": (_sz, [_i64, _i32, _i32]),
     "mx_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "mx_permute_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
@@ -98,6 +99,13 @@ def mx_permute(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows,
     _check(lib().mx_permute(_p(q), _p(s), tokens, cols, _p(expert_ids), topk, num_experts, capacity_rows, _p(q_out),
                             _p(s_out), _p(group_offsets), _p(dst_row), _p(src_row), _p(workspace), workspace_bytes,
                             _s(stream)), "mx_permute")
+
+
+def mx_permute_noalloc(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out,
+                       group_offsets, dst_row, src_row, stream=None):
+    _check(lib().mx_permute_noalloc(_p(q), _p(s), tokens, cols, _p(expert_ids), topk, num_experts, capacity_rows,
+                                    _p(q_out), _p(s_out), _p(group_offsets), _p(dst_row), _p(src_row), _s(stream)),
+           "mx_permute_noalloc")
 
 
 def mx_grouped_gemm_fwd(a_q, a_s, b_q, b_s, group_offsets, num_groups, m_cap, n, k, out, out_dtype, stream=None):

@@ -17,6 +17,8 @@
 //   4. k_permute_tokens copies each token's q/s row once to its topk rows,
 //                     16 B per lane, and zeroes the pad rows.
 
+#include <mutex>
+
 #include "mx_device.h"
 
 namespace mx {
@@ -221,10 +223,12 @@ extern "C" size_t mx_permute_workspace_size(int64_t tokens, int32_t topk, int32_
   return (size_t)(2 * (nt > 0 ? nt : 1) * num_experts) * sizeof(int32_t);
 }
 
-extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
-                          int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,
-                          int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
-                          size_t workspace_bytes, mx_stream_t stream) {
+// Host-side checks of a permute request: the status mx_permute returns
+// before touching the GPU.  Scratch bytes are checked by the callers.
+static int permute_check(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols,
+                         const int32_t* expert_ids, int32_t topk, int32_t num_experts, int64_t capacity_rows,
+                         const uint8_t* q_out, const uint8_t* s_out, const int32_t* group_offsets,
+                         const int32_t* dst_row, const int32_t* src_row) {
   const bool copy = q || s || q_out || s_out;
   if (tokens < 0 || topk < 1 || num_experts < 1) return MX_EINVAL;
   if (num_experts > kMaxExperts) return MX_EUNSUPPORTED;
@@ -234,14 +238,23 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   if (copy && (((uintptr_t)q | (uintptr_t)q_out) & 15)) return MX_EINVAL;  // 16-byte code copies
   const int64_t n = tokens * topk;
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
-  if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (route_tiles(n, num_experts) > 0x7FFFFFFF) return MX_EINVAL;
+  if (copy && tokens + (capacity_rows + 3) / 4 > 0x7FFFFFFF) return MX_EINVAL;  // k_permute_tokens grid
+  return MX_OK;
+}
+
+// The routing kernels and the copy on a checked request; `workspace` holds
+// mx_permute_workspace_size(...) bytes (every byte is written before it is read).
+static int permute_launch(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols,
+                          const int32_t* expert_ids, int32_t topk, int32_t num_experts, int64_t capacity_rows,
+                          uint8_t* q_out, uint8_t* s_out, int32_t* group_offsets, int32_t* dst_row, int32_t* src_row,
+                          int32_t* workspace, hipStream_t st) {
+  const bool copy = q || s || q_out || s_out;
+  const int64_t n = tokens * topk;
   const int32_t tile = route_tile(num_experts);
   const int64_t nt = route_tiles(n, num_experts) > 0 ? route_tiles(n, num_experts) : 1;
-  if (nt > 0x7FFFFFFF) return MX_EINVAL;
-  const int64_t copy_blocks = tokens + (capacity_rows + 3) / 4;  // k_permute_tokens grid
-  if (copy && copy_blocks > 0x7FFFFFFF) return MX_EINVAL;
-  int32_t* hist = static_cast<int32_t*>(workspace);
+  const int64_t copy_blocks = tokens + (capacity_rows + 3) / 4;
+  int32_t* hist = workspace;
   int32_t* base = hist + nt * num_experts;
   const size_t lds = (size_t)num_experts * sizeof(int32_t);  // <= 64 KB (kMaxExperts)
   if (n > 0) {
@@ -261,4 +274,69 @@ extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, in
     hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)copy_blocks), dim3(256), 0, st, q, s, tokens, cols, topk,
                        dst_row, src_row, capacity_rows, q_out, s_out);
   return launch_status();
+}
+
+extern "C" int mx_permute(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols, const int32_t* expert_ids,
+                          int32_t topk, int32_t num_experts, int64_t capacity_rows, uint8_t* q_out, uint8_t* s_out,
+                          int32_t* group_offsets, int32_t* dst_row, int32_t* src_row, void* workspace,
+                          size_t workspace_bytes, mx_stream_t stream) {
+  const int rc = permute_check(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out,
+                               group_offsets, dst_row, src_row);
+  if (rc != MX_OK) return rc;
+  if (!workspace || workspace_bytes < mx_permute_workspace_size(tokens, topk, num_experts)) return MX_EINVAL;
+  return permute_launch(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out, group_offsets,
+                        dst_row, src_row, static_cast<int32_t*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---------------------------------------------------------------------------
+// mx_permute without a caller workspace: the routing tables live in a
+// file-scope device array.  Each GPU holds its own copy; its device address
+// is looked up once per device with hipGetSymbolAddress (the array's name in
+// host code is only a host-side stand-in and is never passed to a kernel).
+
+namespace {
+
+constexpr size_t kScratchBytes = size_t(4) << 20;  // MX_PERMUTE_NOALLOC_SCRATCH_BYTES
+static_assert(kScratchBytes == MX_PERMUTE_NOALLOC_SCRATCH_BYTES, "header and library agree on the scratch size");
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device (set-up on the first call
+// per device), or nullptr with *err set.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" int mx_permute_noalloc(const uint8_t* q, const uint8_t* s, int64_t tokens, int64_t cols,
+                                  const int32_t* expert_ids, int32_t topk, int32_t num_experts, int64_t capacity_rows,
+                                  uint8_t* q_out, uint8_t* s_out, int32_t* group_offsets, int32_t* dst_row,
+                                  int32_t* src_row, mx_stream_t stream) {
+  const int rc = permute_check(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out,
+                               group_offsets, dst_row, src_row);
+  if (rc != MX_OK) return rc;
+  if (mx_permute_workspace_size(tokens, topk, num_experts) > kScratchBytes) return MX_EUNSUPPORTED;
+  hipError_t err = hipSuccess;
+  void* ws = scratch_ptr(&err);
+  if (!ws) return MX_EHIP;
+  return permute_launch(q, s, tokens, cols, expert_ids, topk, num_experts, capacity_rows, q_out, s_out, group_offsets,
+                        dst_row, src_row, static_cast<int32_t*>(ws), reinterpret_cast<hipStream_t>(stream));
 }

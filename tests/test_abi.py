@@ -218,3 +218,17 @@ def test_router_validation(lib):
 def test_python_binding_raises(lib):
     with pytest.raises(mxa.MXError):
         mxa.mx_dequantize(None, None, 4, 32, None, stream=0)
+
+
+def test_permute_noalloc_validation(lib):
+    """The no-allocation permute checks its arguments like mx_permute and
+    rejects requests whose routing tables exceed its built-in scratch, all
+    before touching the GPU."""
+    p = lib.mx_permute_noalloc
+    assert p(P, P, 100, 64, P, 2, 4, 200 + 31 * 4 - 1, P, P, P, P, P, None) == mxa.MX_EINVAL   # capacity
+    assert p(P, P, 100, 64, P, 2, 4, 400, None, P, P, P, P, None) == mxa.MX_EINVAL             # half a copy
+    assert p(Q, P, 100, 64, P, 2, 4, 400, P, P, P, P, P, None) == mxa.MX_EINVAL                # code alignment
+    assert p(None, None, 100, 0, P, 0, 4, 400, None, None, P, P, P, None) == mxa.MX_EINVAL     # topk 0
+    T, E = 1 << 18, 16384
+    assert lib.mx_permute_workspace_size(T, 1, E) > (4 << 20)
+    assert p(None, None, T, 0, P, 1, E, T + 31 * E, None, None, P, P, P, None) == mxa.MX_EUNSUPPORTED
