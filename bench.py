@@ -11,9 +11,16 @@ order, grouped GEMM wgrad; GEMM outputs in bf16.  Inputs are resident in HBM
 before the timed region.
 
 Printed: one JSON line.  ``value`` = GEMM FLOPs of a step (3 x 2*M*N*K over
-the real routed rows) / step time, in TFLOP/s.  ``stages`` gives each stage's
-mean duration (HIP events on the launch stream, every timed step) and its
-throughput against the MI355X peak (MXFP8 dense 5.0 PFLOP/s, HBM 8 TB/s).
+the real routed rows) / step time (the timed region over ``--steps`` steps),
+in TFLOP/s.  ``stages`` gives each stage's median duration (HIP events on
+the launch stream, every timed step; 70 steps, about 0.2 s, by default) and
+its throughput against the MI355X peak (``frac``: MXFP8 dense 5.0 PFLOP/s,
+HBM 8 TB/s) and against the ceilings measured at the start of the run
+(``frac_ceiling``; ``ceilings``: a streaming copy and a scaled-MFMA-only
+loop, kernels of the library).  ``stages_mall_flushed`` times every stage
+again after a 512 MB fill that evicts the Infinity Cache.
+``small_configs`` times the tiny (forward, microseconds) and mid (forward +
+dgrad + wgrad) workloads.
 ``roofline`` reports the dominant GEMM stage.  ``fused_quant_permute`` times
 the same step with the quantize fused into the permute (routing metadata plus
 one gathered row+col quantize of the bf16 tokens in place of the X quantize,
@@ -31,7 +38,8 @@ GEMMs of the same kernel design) and the MXFP8 speedup over it;
 ``graph`` (and ``swiglu_layer.graph``) replays the step captured once in a
 HIP graph.
 ``cpu_baseline`` times the oracle on a bounded sample (three
-median-sized experts' share of the step).
+median-sized experts' share of the step, and the fused quantize of a slice
+of the bandwidth workload), with the host's CPU model and core count.
 """
 
 import argparse
@@ -83,15 +91,21 @@ def ensure_built():
         _build.build()
 
 
-def time_stages(run, names, steps, warmup):
+def time_stages(run, names, steps, warmup, flush=None):
     """Run ``run(name)`` for every name, ``warmup`` untimed then ``steps`` timed
-    passes; per-stage HIP events on torch's current stream (the launch stream)."""
+    passes; per-stage HIP events on torch's current stream (the launch stream).
+    Returns (timed-region ms per pass, per-stage median ms, wall seconds).
+    With ``flush`` (a callable), it runs before every stage, outside the
+    stage's events (and inside the timed region)."""
+    import statistics
+
     import torch
     for _ in range(warmup):
         for n in names:
             run(n)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -99,15 +113,75 @@ def time_stages(run, names, steps, warmup):
     t_start.record()
     for i in range(steps):
         for j, n in enumerate(names):
-            ev[i][j].record()
+            if flush is not None:
+                flush()
+            ev[i][j][0].record()
             run(n)
-        ev[i][-1].record()
+            ev[i][j][1].record()
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    per = {n: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j, n in enumerate(names)}
+    per = {n: statistics.median(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps))
+           for j, n in enumerate(names)}
     return total_ms / steps, per, wall
+
+
+def mall_flusher(nbytes=512 << 20):
+    """A callable that overwrites ``nbytes`` of device memory (a fill kernel):
+    run before a stage, it evicts that stage's inputs from the 256 MB
+    Infinity Cache."""
+    import torch
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    state = {"v": 0}
+
+    def flush():
+        state["v"] ^= 1
+        buf.fill_(state["v"])
+    return flush
+
+
+def measure_ceilings(copy_bytes=1344 << 20, reps=7):
+    """Measured ceilings of this part (library kernels mx_ceiling_copy and
+    mx_ceiling_mfma): the median HBM rate of a streaming copy of
+    ``copy_bytes`` (read + write bytes per second; 2.7 GB moved, the size of
+    the fused quantize's traffic) and the median rate of a loop of scaled
+    FP8 MFMAs at the grouped GEMMs' occupancy (TFLOP/s)."""
+    import statistics
+
+    import torch
+
+    import mxfp8_block_scaled_07_amd as mxa
+    src = torch.ones(copy_bytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    dev = torch.cuda.get_device_properties(0)
+    wgs = dev.multi_processor_count
+    out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
+    iters = 20000
+    mxa.mx_ceiling_copy(src, dst, copy_bytes)
+    mxa.mx_ceiling_mfma(out, wgs, 100)
+    torch.cuda.synchronize()
+    cp, mf = [], []
+    for _ in range(reps):
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        mxa.mx_ceiling_copy(src, dst, copy_bytes)
+        e1.record()
+        mxa.mx_ceiling_mfma(out, wgs, iters)
+        e2.record()
+        torch.cuda.synchronize()
+        cp.append(e0.elapsed_time(e1))
+        mf.append(e1.elapsed_time(e2))
+    flops = wgs * 4 * iters * 16 * 131072.0
+    res = {"hbm_copy_gbps": round(2 * copy_bytes / (statistics.median(cp) * 1e-3) / 1e9, 1),
+           "mfma_mxfp8_tflops": round(flops / (statistics.median(mf) * 1e-3) / 1e12, 1),
+           "copy_bytes_moved": 2 * copy_bytes, "cus": wgs,
+           "note": "medians of 7 launches: mx_ceiling_copy (16-byte non-temporal streaming copy, read + write "
+                   "bytes / time) and mx_ceiling_mfma (16 independent 32x32x64 scaled FP8 MFMAs per wave on "
+                   "register operands, one wave per SIMD)"}
+    del src, dst, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def time_graph(g, steps, warmup):
@@ -127,7 +201,19 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def gpu_expert_path(args, c):
+def stage_entry(n, ms, work, ceil):
+    """Throughput of one stage against the published peak (frac) and the
+    measured ceiling (frac_ceiling)."""
+    if n in work["gemm_flops"]:
+        tf = work["gemm_flops"][n] / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4),
+                "frac_ceiling": round(tf / ceil["mfma_mxfp8_tflops"], 4)}
+    gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
+            "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4)}
+
+
+def gpu_expert_path(args, c, ceil):
     import numpy as np
     import torch
 
@@ -151,15 +237,14 @@ def gpu_expert_path(args, c):
     work = moe.algorithmic_work(T, K, N, E, topk, M)
     stages = {}
     for n in moe.STAGES:
-        ms = per[n]
-        if n in work["gemm_flops"]:
-            tf = work["gemm_flops"][n] / (ms * 1e-3) / 1e12
-            stages[n] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4)}
-        else:
-            gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
-            stages[n] = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+        stages[n] = stage_entry(n, per[n], work, ceil)
         tr = measured_traffic(n)
         stages[n]["traffic"] = None if tr is None else tr["bytes"]
+    # the same stages each timed after evicting the Infinity Cache (a 512 MB
+    # fill before every stage): inputs come from HBM even when they are small
+    _, fper, _ = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), moe.STAGES, max(50, args.steps),
+                             args.warmup, flush=mall_flusher())
+    flushed = {n: stage_entry(n, fper[n], work, ceil) for n in moe.STAGES}
     gemm_total = sum(work["gemm_flops"].values())
     value = gemm_total / (step_ms * 1e-3) / 1e12
     # the same step with the quantize fused into the permute (same bytes out)
@@ -191,11 +276,14 @@ def gpu_expert_path(args, c):
     tr = measured_traffic(dom)
     result = {
         "value": value, "ms_per_step": step_ms, "stages": stages, "wall_s_timed": wall,
+        "stages_mall_flushed": flushed,
         "fused_quant_permute": fused,
         "graph": graph_res,
         "bf16_baseline": bf16,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1), "peak": PEAK_MXFP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_MXFP8_TFLOPS, 4),
+                     "ceiling": ceil["mfma_mxfp8_tflops"],
+                     "frac_ceiling": round(dom_tf / ceil["mfma_mxfp8_tflops"], 4),
                      "traffic": None if tr is None else tr["bytes"],
                      "traffic_detail": tr, "algorithmic_operand_bytes": work["gemm_operand_bytes"][dom],
                      "per_launch_flops": work["gemm_flops"][dom], "avg_launch_ms": round(per[dom], 4)},
@@ -248,7 +336,57 @@ def gpu_bf16_step(args, c, x, w, dy, ids, work, mx_step_ms, mx_per):
                     "(the columnwise quantizes' counterparts), bf16-MFMA grouped GEMMs of the same kernel design"}
 
 
-def gpu_quantize_bandwidth(args):
+def gpu_small_configs(args, ceil):
+    """The tiny and mid workloads of the benchmark specification, timed like
+    the headline step (medians over >= 50 passes): the tiny case forward only
+    (E=4, K=256, N=512, 2048 rows, fp32 output; its kernels are launch-bound,
+    so it is reported in microseconds) and the mid case forward + dgrad +
+    wgrad (E=8, K=2048, N=1408, 16384 Zipf-sized rows, bf16 outputs)."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from mxfp8_block_scaled_07_amd import MX_OUT_BF16, MX_OUT_F32, moe
+
+    out = {}
+    for cfg, stages, od in ((1, ("quant_x", "permute", "quant_w", "gemm_fwd"), MX_OUT_F32),
+                            (2, moe.STAGES, MX_OUT_BF16)):
+        c = workloads.config(cfg)
+        T, K, N, E, topk = c["T"], c["K"], c["N"], c["E"], c["topk"]
+        dev = "cuda:0"
+        x = torch.from_numpy(c["x"].view(np.int16)).to(dev)
+        w = torch.from_numpy(c["w"].view(np.int16)).to(dev)
+        ids = torch.from_numpy(c["expert_ids"].astype(np.int32)).to(dev)
+        b = moe.ExpertBuffers(T, K, N, E, topk, device=dev, out_dtype=od)
+        dy = None
+        if "dy_full" in c:
+            moe.run_stage("quant_x", b, x, w, None, ids)
+            moe.run_stage("permute", b, x, w, None, ids)
+            dy = moe.zero_pad_rows(torch.from_numpy(c["dy_full"].view(np.int16)).to(dev), b.src)
+        torch.cuda.synchronize()
+        step_ms, per, _ = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), stages, max(50, args.steps),
+                                      args.warmup)
+        work = moe.algorithmic_work(T, K, N, E, topk)
+        st = {n: stage_entry(n, per[n], work, ceil) for n in stages}
+        for n in st:
+            st[n]["us"] = round(per[n] * 1e3, 2)
+        flops = sum(work["gemm_flops"][n] for n in stages if n in work["gemm_flops"])
+        gemm_ms = sum(per[n] for n in stages if n in work["gemm_flops"])
+        out[f"config{cfg}"] = {
+            "workload": ("tiny expert GEMM fwd: E=4, K=256, N=512, 2048 rows, fp32 output" if cfg == 1 else
+                         "mid expert layer fwd+dgrad+wgrad: E=8, K=2048, N=1408, 16384 Zipf(1.2)-sized rows, "
+                         "bf16 outputs"),
+            "us_per_step": round(step_ms * 1e3, 2), "gemm_us": round(gemm_ms * 1e3, 2),
+            "gemm_tflops": round(flops / (gemm_ms * 1e-3) / 1e12, 1),
+            "gemm_frac": round(flops / (gemm_ms * 1e-3) / 1e12 / PEAK_MXFP8_TFLOPS, 4), "stages": st}
+        del b, x, w, dy
+        torch.cuda.empty_cache()
+    out["note"] = ("the tiny case's GEMM is 0.54 GFLOP, far below one launch's latency: its fraction of the "
+                   "peak is not meaningful and is reported for completeness")
+    return out
+
+
+def gpu_quantize_bandwidth(args, ceil):
     import numpy as np
     import torch
 
@@ -272,14 +410,15 @@ def gpu_quantize_bandwidth(args):
             mxa.mx_dequantize(qt, st, cols, rows, yt)
 
     names = ("quant_rowcol", "dequant_row", "dequant_col")
-    _, per, _ = time_stages(run, names, max(5, args.steps // 2), 2)
+    _, per, _ = time_stages(run, names, max(50, args.steps), 2)
     n_el = rows * cols
     nbytes = {"quant_rowcol": n_el * (2 + 2 * (1 + 1 / 32)), "dequant_row": n_el * (1 + 1 / 32 + 2),
               "dequant_col": n_el * (1 + 1 / 32 + 2)}
     out = {}
     for n in names:
         gbs = nbytes[n] / (per[n] * 1e-3) / 1e9
-        out[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4)}
+        out[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
+                  "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4)}
     out["shape"] = [rows, cols]
     del x, q, s, qt, st, y, yt
     torch.cuda.empty_cache()
@@ -416,6 +555,17 @@ def copy_calibration():
     torch.cuda.empty_cache()
 
 
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), else the machine type."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(args, c):
     """The oracle, as it stands, on three experts' share of the step (about
     10-20 s of host work)."""
@@ -456,9 +606,22 @@ def cpu_baseline(args, c):
     dt = time.perf_counter() - t0
     flops = 3 * 2.0 * m * c["N"] * c["K"]
     cores = len(os.sched_getaffinity(0))
+    # the oracle's fused rowwise + columnwise quantize on a slice of the
+    # bandwidth workload's tensor (2048 of its 131072 rows, same recipe)
+    import workloads
+    qrows, qcols = 2048, 5120
+    xq = workloads.quant_tensor(4, qrows, qcols)
+    tq = time.perf_counter()
+    mx.quantize_rowwise(xq)
+    mx.quantize_colwise(xq)
+    dq = time.perf_counter() - tq
+    qgbps = qrows * qcols * (2 + 2 * (1 + 1 / 32)) / dq / 1e9
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": blas_threads or cores,
             "host_cores": cores, "kind": "oracle", "seconds": round(dt, 2),
-            "cpu": platform.processor() or platform.machine(),
+            "cpu": cpu_model(),
+            "quantize_gbps": round(qgbps, 3), "quantize_seconds": round(dq, 2),
+            "quantize_sample": f"oracle rowwise + columnwise quantize of a [{qrows}, {qcols}] slice of the "
+                               f"bandwidth workload (same recipe; 4.0625 B per element), one process",
             "sample": f"three median-sized experts ({m} routed rows of 16384): routing of all 8192x2 ids, and "
                       f"per expert the rowwise/colwise quantize of its X rows, W_e and dY rows, its permute and "
                       f"the fp64 fwd/dgrad/wgrad GEMMs (value = their GEMM FLOPs / wall time)"}
@@ -467,7 +630,7 @@ def cpu_baseline(args, c):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=70)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quant-bench", action="store_true")
@@ -482,17 +645,19 @@ def main():
     ensure_built()
     import workloads
     c = workloads.config(3)
-    res = gpu_expert_path(args, c)
+    ceil = measure_ceilings()
+    res = gpu_expert_path(args, c, ceil)
     line = {
         "metric": METRIC, "value": round(res["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(res["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "mxfp8", "data": "synthetic",
         "config": res["config"], "roofline": res["roofline"], "stages": res["stages"],
         "fused_quant_permute": res["fused_quant_permute"], "graph": res["graph"],
-        "bf16_baseline": res["bf16_baseline"],
+        "bf16_baseline": res["bf16_baseline"], "ceilings": ceil, "stages_mall_flushed": res["stages_mall_flushed"],
     }
     if not args.no_quant_bench:
-        line["quantize_bandwidth"] = gpu_quantize_bandwidth(args)
+        line["quantize_bandwidth"] = gpu_quantize_bandwidth(args, ceil)
+    line["small_configs"] = gpu_small_configs(args, ceil)
     if not args.no_layer:
         line["swiglu_layer"] = gpu_swiglu_layer(args)
     if args.copy_calibration:

@@ -329,6 +329,24 @@ int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const in
                                int32_t num_groups, int64_t m_cap, int64_t n, int64_t k, void* dw, int32_t out_dtype,
                                mx_stream_t stream);
 
+/*
+ * Measurement helpers (not part of the MXFP8 path): the ceilings the
+ * benchmark reports its roofline fractions against, next to the published
+ * peaks.
+ *
+ * mx_ceiling_copy: a streaming copy of `bytes` (a multiple of 16384; src
+ *   and dst 16-byte aligned device buffers that do not overlap), 16-byte
+ *   non-temporal loads and stores -- the HBM read + write rate an HBM-bound
+ *   kernel can reach.
+ * mx_ceiling_mfma: `workgroups` workgroups of 256 threads, each wave running
+ *   `iters` rounds of 16 independent V_MFMA_SCALE_F32_32X32X64_F8F6F4 on
+ *   register operands (one wave per SIMD, the grouped GEMM's occupancy); it
+ *   performs workgroups * 4 * iters * 16 * 131072 FLOPs and writes one float
+ *   per thread to out [workgroups * 256].
+ */
+int mx_ceiling_copy(const void* src, void* dst, int64_t bytes, mx_stream_t stream);
+int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, mx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

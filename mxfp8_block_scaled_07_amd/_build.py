@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxmoe.so")
-SOURCES = ["quantize.hip", "permute.hip", "gemm.hip", "glue.hip", "router.hip", "bf16.hip"]
+SOURCES = ["quantize.hip", "permute.hip", "gemm.hip", "glue.hip", "router.hip", "bf16.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
