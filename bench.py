@@ -146,7 +146,9 @@ def measure_ceilings(copy_bytes=1344 << 20, reps=7):
     mx_ceiling_mfma): the median HBM rate of a streaming copy of
     ``copy_bytes`` (read + write bytes per second; 2.7 GB moved, the size of
     the fused quantize's traffic) and the median rate of a loop of scaled
-    FP8 MFMAs at the grouped GEMMs' occupancy (TFLOP/s)."""
+    FP8 MFMAs in the grouped GEMMs' register pattern, on random operands (the
+    rate the part sustains on real data: their switching power lowers the
+    clock) and on near-constant operands (TFLOP/s)."""
     import statistics
 
     import torch
@@ -159,46 +161,35 @@ def measure_ceilings(copy_bytes=1344 << 20, reps=7):
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
     iters = 20000
     mxa.mx_ceiling_copy(src, dst, copy_bytes)
-    mxa.mx_ceiling_mfma(out, wgs, 100)
+    mxa.mx_ceiling_mfma(out, wgs, 100, True)
     torch.cuda.synchronize()
-    cp, mf = [], []
+    cp, mf, mc = [], [], []
     for _ in range(reps):
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        e0.record()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
         mxa.mx_ceiling_copy(src, dst, copy_bytes)
-        e1.record()
-        mxa.mx_ceiling_mfma(out, wgs, iters)
-        e2.record()
+        e[1].record()
+        mxa.mx_ceiling_mfma(out, wgs, iters, True)
+        e[2].record()
+        mxa.mx_ceiling_mfma(out, wgs, iters, False)
+        e[3].record()
         torch.cuda.synchronize()
-        cp.append(e0.elapsed_time(e1))
-        mf.append(e1.elapsed_time(e2))
+        cp.append(e[0].elapsed_time(e[1]))
+        mf.append(e[1].elapsed_time(e[2]))
+        mc.append(e[2].elapsed_time(e[3]))
     flops = wgs * 4 * iters * 16 * 131072.0
     res = {"hbm_copy_gbps": round(2 * copy_bytes / (statistics.median(cp) * 1e-3) / 1e9, 1),
            "mfma_mxfp8_tflops": round(flops / (statistics.median(mf) * 1e-3) / 1e12, 1),
+           "mfma_mxfp8_tflops_constant_operands": round(flops / (statistics.median(mc) * 1e-3) / 1e12, 1),
            "copy_bytes_moved": 2 * copy_bytes, "cus": wgs,
            "note": "medians of 7 launches: mx_ceiling_copy (16-byte non-temporal streaming copy, read + write "
-                   "bytes / time) and mx_ceiling_mfma (16 independent 32x32x64 scaled FP8 MFMAs per wave on "
-                   "register operands, one wave per SIMD)"}
+                   "bytes / time) and mx_ceiling_mfma (16 independent 32x32x64 scaled FP8 MFMAs per wave on the GEMM "
+                   "step's 4 A + 4 B register fragments, one wave per SIMD); mfma_mxfp8_tflops uses random codes "
+                   "and scales (the ceiling on real data), the constant-operand figure shows the clock headroom "
+                   "that data-dependent power takes away"}
     del src, dst, out
     torch.cuda.empty_cache()
     return res
-
-
-def time_graph(g, steps, warmup):
-    """ms per replay of a captured step: ``warmup`` untimed replays, then
-    ``steps`` replays between two events on torch's current stream."""
-    import torch
-    for _ in range(warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
 
 
 def stage_entry(n, ms, work, ceil):

@@ -340,12 +340,15 @@ int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const in
  *   kernel can reach.
  * mx_ceiling_mfma: `workgroups` workgroups of 256 threads, each wave running
  *   `iters` rounds of 16 independent V_MFMA_SCALE_F32_32X32X64_F8F6F4 on
- *   register operands (one wave per SIMD, the grouped GEMM's occupancy); it
- *   performs workgroups * 4 * iters * 16 * 131072 FLOPs and writes one float
- *   per thread to out [workgroups * 256].
+ *   register operands in the grouped GEMM's register pattern (4 A and 4 B
+ *   fragments, one wave per SIMD); random_operands != 0 fills them with
+ *   random E4M3 codes and scale bytes (the switching power of real data,
+ *   which lowers the clock the part sustains), 0 with near-constant codes.
+ *   It performs workgroups * 4 * iters * 16 * 131072 FLOPs and writes one
+ *   float per thread to out [workgroups * 256].
  */
 int mx_ceiling_copy(const void* src, void* dst, int64_t bytes, mx_stream_t stream);
-int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, mx_stream_t stream);
+int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, int32_t random_operands, mx_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ _SIGNATURES = {
     "mx_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mx_permute_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mx_ceiling_copy": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
-    "mx_ceiling_mfma": (ctypes.c_int, [_vp, _i32, _i32, _vp]),
+    "mx_ceiling_mfma": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
@@ -114,8 +114,9 @@ def mx_ceiling_copy(src, dst, nbytes, stream=None):
     _check(lib().mx_ceiling_copy(_p(src), _p(dst), nbytes, _s(stream)), "mx_ceiling_copy")
 
 
-def mx_ceiling_mfma(out, workgroups, iters, stream=None):
-    _check(lib().mx_ceiling_mfma(_p(out), workgroups, iters, _s(stream)), "mx_ceiling_mfma")
+def mx_ceiling_mfma(out, workgroups, iters, random_operands=True, stream=None):
+    _check(lib().mx_ceiling_mfma(_p(out), workgroups, iters, int(bool(random_operands)), _s(stream)),
+           "mx_ceiling_mfma")
 
 
 def mx_grouped_gemm_fwd(a_q, a_s, b_q, b_s, group_offsets, num_groups, m_cap, n, k, out, out_dtype, stream=None):

@@ -25,31 +25,62 @@ __global__ void __launch_bounds__(256) k_copy(const v4u* __restrict__ src, v4u* 
   for (int i = 0; i < 4; ++i) __builtin_nontemporal_store(v[i], dst + base + 256 * i);
 }
 
+// A random E4M3 code in every byte (no NaN code), random signs.
+__device__ __forceinline__ int random_codes(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352dU; x ^= x >> 15; x *= 0x846ca68bU; x ^= x >> 16;
+  uint32_t out = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    uint32_t c = (x >> (8 * b)) & 0xFF;
+    if ((c & 0x7F) >= 0x7E) c &= 0xF7;
+    out |= c << (8 * b);
+  }
+  return (int)out;
+}
+
 // One 256-thread workgroup per CU (one wave per SIMD, as the grouped GEMM
-// runs), 16 independent 32x32x64 accumulators per wave (the GEMM's 4 x 4
-// tiles), `iters` rounds of 16 scaled MFMAs on operands held in registers.
+// runs), the GEMM step's register pattern: 4 A and 4 B fragments and their
+// scale bytes, 4 x 4 accumulators of 32 x 32, `iters` rounds of 16 scaled
+// MFMAs with no memory traffic.  With kRandom the fragments hold random
+// codes and scales (the power the GEMMs draw on real data, which sets the
+// clock the part holds); otherwise near-constant codes.
+template <bool kRandom>
 __global__ void __launch_bounds__(256) k_mfma_loop(float* __restrict__ out, int32_t iters) {
   const int lane = threadIdx.x & 63;
-  v8i a, b;
+  const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 977u;
+  v8i a[4], b[4];
+  int sa[4], sb[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    a[i] = 0x38383838 ^ ((lane + i) & 7);      // E4M3 codes near 1.0
-    b[i] = 0x30303030 ^ ((lane * 3 + i) & 7);  // near 0.25
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      a[i][q] = kRandom ? random_codes(seed + 16 * i + q) : 0x38383838 ^ ((lane + q) & 7);
+      b[i][q] = kRandom ? random_codes(seed + 16 * i + q + 1000003u) : 0x30303030 ^ ((lane * 3 + q) & 7);
+    }
+    sa[i] = kRandom ? 118 + (int)(seed * (i + 3) >> 28) : 127;
+    sb[i] = kRandom ? 118 + (int)(seed * (i + 7) >> 28) : 100;
   }
-  v16f acc[16];
+  v16f acc[4][4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   for (int32_t it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[j], 0, 0, 0, 127, 0, 100);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[j], a[i], acc[i][j], 0, 0, 0, sb[j], 0, sa[i]);
   }
   float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s += acc[j][r];
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += acc[i][j][r];
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
@@ -68,9 +99,13 @@ extern "C" int mx_ceiling_copy(const void* src, void* dst, int64_t bytes, mx_str
   return launch_status();
 }
 
-extern "C" int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, mx_stream_t stream) {
+extern "C" int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, int32_t random_operands,
+                               mx_stream_t stream) {
   if (!out || workgroups < 1 || iters < 1) return MX_EINVAL;
-  hipLaunchKernelGGL(k_mfma_loop, dim3((unsigned)workgroups), dim3(256), 0, reinterpret_cast<hipStream_t>(stream),
-                     out, iters);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (random_operands)
+    hipLaunchKernelGGL(k_mfma_loop<true>, dim3((unsigned)workgroups), dim3(256), 0, st, out, iters);
+  else
+    hipLaunchKernelGGL(k_mfma_loop<false>, dim3((unsigned)workgroups), dim3(256), 0, st, out, iters);
   return launch_status();
 }
