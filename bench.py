@@ -192,6 +192,23 @@ def measure_ceilings(copy_bytes=1344 << 20, reps=7):
     return res
 
 
+def time_graph(g, steps, warmup):
+    """ms per replay of a captured step: ``warmup`` untimed replays, then
+    ``steps`` replays between two events on torch's current stream."""
+    import torch
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def stage_entry(n, ms, work, ceil):
     """Throughput of one stage against the published peak (frac) and the
     measured ceiling (frac_ceiling)."""
