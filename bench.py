@@ -60,6 +60,26 @@ METRIC = "MXFP8 grouped-GEMM TFLOP/s fwd+bwd and quantize GB/s, % of MI355X peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 CALIB_BYTES = 1 << 30        # plain device copy used to scale the FETCH_SIZE / WRITE_SIZE counters
 
+# Counter pass (--counter-pass): every stage runs COUNTER_REPS times, each
+# launch bracketed by marker kernels, so that per-dispatch hardware counters
+# (rocprofv3 --pmc) can be attributed to stages by position alone.
+COUNTER = None
+COUNTER_REPS = 3
+MARKER_KERNEL = "FillFunctor<long>"   # the marker: a one-element int64 fill (nothing else on the path fills int64)
+
+
+def counter_mark(label):
+    """Counter pass: launch the marker kernel; the launches up to the next
+    marker belong to ``label``."""
+    COUNTER["labels"].append(label)
+    COUNTER["marker"].fill_(len(COUNTER["labels"]))
+
+
+def counter_work(prefix, nbytes):
+    """Counter pass: record the algorithmic bytes of the stages ``prefix + name``."""
+    if COUNTER is not None:
+        COUNTER["alg"].update({prefix + n: float(v) for n, v in nbytes.items()})
+
 
 def measured_traffic(stage):
     """HBM bytes per launch of ``stage`` as recorded in profiles/hbm_traffic.txt
@@ -91,15 +111,28 @@ def ensure_built():
         _build.build()
 
 
-def time_stages(run, names, steps, warmup, flush=None):
+def time_stages(run, names, steps, warmup, flush=None, label=""):
     """Run ``run(name)`` for every name, ``warmup`` untimed then ``steps`` timed
     passes; per-stage HIP events on torch's current stream (the launch stream).
     Returns (timed-region ms per pass, per-stage median ms, wall seconds).
     With ``flush`` (a callable), it runs before every stage, outside the
-    stage's events (and inside the timed region)."""
+    stage's events (and inside the timed region).  In the counter pass each
+    stage instead runs COUNTER_REPS times between markers labelled
+    ``label + name`` (the cache-flushed passes are skipped) and the times
+    returned are placeholders."""
     import statistics
 
     import torch
+    if COUNTER is not None:
+        if flush is None:
+            print(f"counter pass: {label}{names[0]} .. {names[-1]}", file=sys.stderr, flush=True)
+            for _ in range(COUNTER_REPS):
+                for n in names:
+                    counter_mark(label + n)
+                    run(n)
+                    counter_mark("other")
+            torch.cuda.synchronize()
+        return 1.0, {n: 1.0 for n in names}, 0.0
     for _ in range(warmup):
         for n in names:
             run(n)
@@ -196,6 +229,8 @@ def time_graph(g, steps, warmup):
     """ms per replay of a captured step: ``warmup`` untimed replays, then
     ``steps`` replays between two events on torch's current stream."""
     import torch
+    if COUNTER is not None:
+        return 1.0
     for _ in range(warmup):
         g.replay()
     torch.cuda.synchronize()
@@ -243,6 +278,8 @@ def gpu_expert_path(args, c, ceil):
     step_ms, per, wall = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), moe.STAGES, args.steps,
                                      args.warmup)
     work = moe.algorithmic_work(T, K, N, E, topk, M)
+    for pre in ("", "fused."):
+        counter_work(pre, {**work["bytes"], **work["gemm_operand_bytes"]})
     stages = {}
     for n in moe.STAGES:
         stages[n] = stage_entry(n, per[n], work, ceil)
@@ -257,7 +294,7 @@ def gpu_expert_path(args, c, ceil):
     value = gemm_total / (step_ms * 1e-3) / 1e12
     # the same step with the quantize fused into the permute (same bytes out)
     f_ms, f_per, _ = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), moe.FUSED_STAGES, args.steps,
-                                 args.warmup)
+                                 args.warmup, label="fused.")
     fused_stages = {}
     for n in moe.FUSED_STAGES:
         if n in work["gemm_flops"]:
@@ -272,7 +309,7 @@ def gpu_expert_path(args, c, ceil):
                      "the MXFP8 permute and quant_xt; bit-identical results"}
     # the same step captured once in a HIP graph and replayed (no host launch
     # gaps, no per-stage events)
-    graph = moe.capture(lambda: moe.expert_step(b, x, w, dy, ids))
+    graph = None if COUNTER is not None else moe.capture(lambda: moe.expert_step(b, x, w, dy, ids))
     g_ms = time_graph(graph, args.steps, args.warmup)
     del graph
     graph_res = {"ms_per_step": round(g_ms, 4), "tflops": round(sum(work["gemm_flops"].values()) / (g_ms * 1e-3) / 1e12, 1),
@@ -319,8 +356,9 @@ def gpu_bf16_step(args, c, x, w, dy, ids, work, mx_step_ms, mx_per):
     T, K, N, E, topk = c["T"], c["K"], c["N"], c["E"], c["topk"]
     b = moe.Bf16Buffers(T, K, N, E, topk, device="cuda:0", out_dtype=MX_OUT_BF16)
     ms, per, _ = time_stages(lambda n: moe.run_bf16_stage(n, b, x, w, dy, ids), moe.BF16_STAGES, args.steps,
-                             args.warmup)
+                             args.warmup, label="bf16.")
     bw = moe.bf16_work(T, K, N, E, topk)
+    counter_work("bf16.", {**bw["bytes"], **bw["gemm_operand_bytes"]})
     stages = {}
     for n in moe.BF16_STAGES:
         if n in work["gemm_flops"]:
@@ -373,7 +411,7 @@ def gpu_small_configs(args, ceil):
             dy = moe.zero_pad_rows(torch.from_numpy(c["dy_full"].view(np.int16)).to(dev), b.src)
         torch.cuda.synchronize()
         step_ms, per, _ = time_stages(lambda n: moe.run_stage(n, b, x, w, dy, ids), stages, max(50, args.steps),
-                                      args.warmup)
+                                      args.warmup, label=f"config{cfg}.")
         work = moe.algorithmic_work(T, K, N, E, topk)
         st = {n: stage_entry(n, per[n], work, ceil) for n in stages}
         for n in st:
@@ -418,15 +456,17 @@ def gpu_quantize_bandwidth(args, ceil):
             mxa.mx_dequantize(qt, st, cols, rows, yt)
 
     names = ("quant_rowcol", "dequant_row", "dequant_col")
-    _, per, _ = time_stages(run, names, max(50, args.steps), 2)
+    _, per, _ = time_stages(run, names, max(50, args.steps), 2, label="quant.")
     n_el = rows * cols
     nbytes = {"quant_rowcol": n_el * (2 + 2 * (1 + 1 / 32)), "dequant_row": n_el * (1 + 1 / 32 + 2),
               "dequant_col": n_el * (1 + 1 / 32 + 2)}
     out = {}
     for n in names:
         gbs = nbytes[n] / (per[n] * 1e-3) / 1e9
+        tr = measured_traffic("quant." + n)
         out[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
-                  "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4)}
+                  "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4), "traffic": None if tr is None else tr["bytes"]}
+    counter_work("quant.", nbytes)
     out["shape"] = [rows, cols]
     del x, q, s, qt, st, y, yt
     torch.cuda.empty_cache()
@@ -453,8 +493,10 @@ def gpu_swiglu_layer(args):
     torch.cuda.synchronize()
     steps = max(3, args.steps // 4)
     step_ms, per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, logits, dout),
-                                  moe.LAYER_STAGES, steps, 2)
+                                  moe.LAYER_STAGES, steps, 2, label="layer.")
     work = moe.layer_work(T, H, F, E, k)
+    for pre in ("layer.", "layer_fused."):
+        counter_work(pre, {**work["bytes"], **work["gemm_operand_bytes"]})
     stages = {}
     for n in moe.LAYER_STAGES:
         ms = per[n]
@@ -475,13 +517,13 @@ def gpu_swiglu_layer(args):
            "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4), "stages": stages}
     # the same layer with the quantize fused into the permute (same bytes out)
     f_ms, f_per, _ = time_stages(lambda n: moe.run_layer_stage(n, b, x, w1, w2, logits, dout),
-                                 moe.LAYER_FUSED_STAGES, steps, 2)
+                                 moe.LAYER_FUSED_STAGES, steps, 2, label="layer_fused.")
     res["fused_quant_permute"] = {
         "ms_per_step": round(f_ms, 3), "tflops": round(flops / (f_ms * 1e-3) / 1e12, 1),
         "stages": {n: {"ms": round(f_per[n], 4), "gbps": round(work["bytes"][n] / (f_per[n] * 1e-3) / 1e9, 1)}
                    for n in ("route", "quant_xperm")},
         "replaces": {n: round(per[n], 4) for n in ("quant_x", "permute", "quant_xt")}}
-    graph = moe.capture(lambda: moe.layer_step(b, x, w1, w2, logits, dout))
+    graph = None if COUNTER is not None else moe.capture(lambda: moe.layer_step(b, x, w1, w2, logits, dout))
     g_ms = time_graph(graph, steps, 2)
     del graph
     res["graph"] = {"ms_per_step": round(g_ms, 3), "tflops": round(flops / (g_ms * 1e-3) / 1e12, 1)}
@@ -531,8 +573,14 @@ def layer_bf16_gemms(args, b, x, w1, w2, mx_per, work):
             mxa.mx_bf16_grouped_gemm_wgrad(dht, xt, b.off, E, cap, 2 * F, H, o_dw1, out)
 
     names = ("gemm1_fwd", "gemm2_fwd", "gemm2_dgrad", "gemm2_wgrad", "gemm1_dgrad", "gemm1_wgrad")
+    M = T * b.topk   # routed rows: every token goes to topk experts
+    counter_work("layer_bf16.", {   # bf16 operands read once, bf16 output written once
+        "gemm1_fwd": (M * H + E * 2 * F * H) * 2 + M * 2 * F * 2, "gemm2_fwd": (M * F + E * H * F) * 2 + M * H * 2,
+        "gemm2_dgrad": (M * H + E * F * H) * 2 + M * F * 2, "gemm2_wgrad": (H * M + F * M) * 2 + E * H * F * 2,
+        "gemm1_dgrad": (M * 2 * F + E * H * 2 * F) * 2 + M * H * 2,
+        "gemm1_wgrad": (2 * F * M + H * M) * 2 + E * 2 * F * H * 2})
     torch.cuda.synchronize()
-    _, per, _ = time_stages(run, names, max(3, args.steps // 4), 2)
+    _, per, _ = time_stages(run, names, max(3, args.steps // 4), 2, label="layer_bf16.")
     stages = {}
     for n in names:
         tf = work["gemm_flops"][n] / (per[n] * 1e-3) / 1e12
@@ -557,7 +605,11 @@ def copy_calibration():
     b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
+        if COUNTER is not None:
+            counter_mark("calibration")
         b.copy_(a)
+        if COUNTER is not None:
+            counter_mark("other")
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
@@ -635,6 +687,99 @@ def cpu_baseline(args, c):
                       f"the fp64 fwd/dgrad/wgrad GEMMs (value = their GEMM FLOPs / wall time)"}
 
 
+# kernel sources behind each stage (the traffic record hashes them)
+_CS = "mxfp8_block_scaled_07_amd/csrc/"
+_SRC_QUANT = [_CS + "quantize.hip", _CS + "tile_quant.h", _CS + "mx_device.h"]
+
+
+def stage_sources(label):
+    pre, n = label.rsplit(".", 1) if "." in label else ("", label)
+    if n.startswith("gemm"):
+        return [_CS + "gemm.hip"]
+    if n in ("permute", "route"):
+        return [_CS + "permute.hip"]
+    if pre in ("bf16", "layer_bf16") or n == "permute_bf16" or n.startswith("transpose"):
+        return [_CS + "bf16.hip", _CS + "mx_device.h"]
+    if n in ("router", "router_bwd"):
+        return [_CS + "router.hip", _CS + "mx_device.h"]
+    if n in ("swiglu", "swiglu_bwd", "combine", "combine_bwd", "unpermute_dx"):
+        return [_CS + "glue.hip", _CS + "tile_quant.h", _CS + "mx_device.h"]
+    return _SRC_QUANT
+
+
+def summarize_counters(fetch_csv, write_csv, log, out_path=TRAFFIC_FILE):
+    """Write profiles/hbm_traffic.txt from two counter passes (FETCH_SIZE and
+    WRITE_SIZE, one counter each) and the counter pass's printed line: the
+    dispatches between two markers are one call of the stage the first marker
+    names; a stage's bytes are the mean over its calls of the summed counter
+    (KiB) of its dispatches, scaled by what the same counter reads for a plain
+    copy of CALIB_BYTES."""
+    import csv
+    import statistics
+
+    info = [json.loads(ln) for ln in open(log) if ln.startswith('{"counter_pass"')][-1]["counter_pass"]
+    labels, alg = info["labels"], info["algorithmic_bytes"]
+
+    def per_label(path):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        calls, cur, n_mark = {}, None, 0
+        for r in rows:
+            if MARKER_KERNEL in r["Kernel_Name"]:
+                if n_mark == len(labels):
+                    raise SystemExit(f"{path}: more marker dispatches than the {len(labels)} labels")
+                if cur is not None:
+                    calls.setdefault(cur[0], []).append(cur[1])
+                cur = [labels[n_mark], 0.0]
+                n_mark += 1
+            elif cur is not None:
+                cur[1] += float(r["Counter_Value"])
+        if cur is not None:
+            calls.setdefault(cur[0], []).append(cur[1])
+        if n_mark != len(labels):
+            raise SystemExit(f"{path}: {n_mark} marker dispatches for {len(labels)} labels")
+        return {k: statistics.fmean(v) for k, v in calls.items()}
+
+    f, w = per_label(fetch_csv), per_label(write_csv)
+    ff, fw = CALIB_BYTES / (f["calibration"] * 1024), CALIB_BYTES / (w["calibration"] * 1024)
+    cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 900 rocprofv3 --pmc {C} -d $GRAFT_REPO_ROOT/gpurun_out/"
+           "pmc_{c} -o run --output-format csv -- python3 $GRAFT_REPO_ROOT/bench.py --counter-pass "
+           "> $GRAFT_REPO_ROOT/gpurun_out/pmc_{c}.log")
+    out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE): expert step, large workload",
+           "# (T=8192, K=5120, N=8192, E=16, top-2); fused. the same step with the quantize fused into the",
+           "# permute; bf16. its BF16 baseline; quant. the quantize-bandwidth tensor [131072, 5120]; layer. the",
+           "# SwiGLU expert FFN layer (T=32768, top-8 of E=64, hidden 7168, ffn 2048), layer_fused. with the",
+           "# fused permute, layer_bf16. its six GEMMs on bf16 operands.",
+           "#",
+           "# Commands (from the repository root on one MI355X), one counter per run, then the summary:",
+           "#   " + cmd.format(C="FETCH_SIZE", c="fetch"),
+           "#   " + cmd.format(C="WRITE_SIZE", c="write"),
+           "#   python3 bench.py --summarize-counters gpurun_out/pmc_fetch/run_counter_collection.csv "
+           "gpurun_out/pmc_write/run_counter_collection.csv gpurun_out/pmc_fetch.log",
+           "#",
+           f"# The counter pass runs every stage {info['reps']} times, each call between two marker kernels",
+           "#   (one-element int64 fills); a stage's bytes are the mean over its calls of the counter summed",
+           "#   over the call's dispatches (KiB) x 1024 x the calibration factor.",
+           f"# Calibration: a plain copy of {CALIB_BYTES} bytes reads FETCH_SIZE {f['calibration']:.0f} KiB and",
+           f"#   WRITE_SIZE {w['calibration']:.0f} KiB per launch; factors fetch x{ff:.4f}, write x{fw:.4f}.",
+           "# algorithmic = bytes the stage must move at least once (moe.algorithmic_work, bf16_work,",
+           "#   layer_work); GEMM stages count their operands and bf16 output once.",
+           "# sha256 = of the kernel sources (in the order listed) when the counters were taken; bench.py ignores",
+           "#   a record whose sources changed.",
+           "#"]
+    for lab in dict.fromkeys(labels):
+        if lab in ("other", "calibration") or lab.startswith("config") or lab not in f or lab not in w:
+            continue
+        fb, wb = f[lab] * 1024 * ff, w[lab] * 1024 * fw
+        srcs = stage_sources(lab)
+        digest = hashlib.sha256(b"".join(open(os.path.join(ROOT, x), "rb").read() for x in srcs)).hexdigest()
+        a = alg.get(lab)
+        ratio = f"{(fb + wb) / a:.3f}" if a else "n/a"
+        out.append(f"stage={lab} source={','.join(srcs)} sha256={digest} fetch_bytes={fb:.0f} write_bytes={wb:.0f} "
+                   f"algorithmic_bytes={a or 0:.0f} ratio={ratio}")
+    open(out_path, "w").write("\n".join(out) + "\n")
+    print(f"wrote {out_path}: {len(out)} lines")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -645,7 +790,16 @@ def main():
     ap.add_argument("--no-layer", action="store_true", help="skip the SwiGLU expert FFN layer workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-small-configs", action="store_true", help="skip the tiny and mid workloads")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="run every stage a few times between marker kernels, for per-stage hardware counters "
+                         "(rocprofv3 --pmc); prints the stage labels instead of timings")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LOG"),
+                    help="write profiles/hbm_traffic.txt from two counter passes (no GPU needed)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the expert path has no multi-GPU leg "
               "(run with --gpus 1)", file=sys.stderr)
@@ -653,7 +807,13 @@ def main():
     ensure_built()
     import workloads
     c = workloads.config(3)
-    ceil = measure_ceilings()
+    if args.counter_pass:
+        import torch
+        global COUNTER
+        COUNTER = {"labels": [], "alg": {}, "marker": torch.empty(1, dtype=torch.int64, device="cuda:0")}
+        ceil = {"hbm_copy_gbps": 1.0, "mfma_mxfp8_tflops": 1.0, "mfma_mxfp8_tflops_constant_operands": 1.0}
+    else:
+        ceil = measure_ceilings()
     res = gpu_expert_path(args, c, ceil)
     line = {
         "metric": METRIC, "value": round(res["value"], 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -665,11 +825,16 @@ def main():
     }
     if not args.no_quant_bench:
         line["quantize_bandwidth"] = gpu_quantize_bandwidth(args, ceil)
-    line["small_configs"] = gpu_small_configs(args, ceil)
+    if not (args.no_small_configs or args.counter_pass):
+        line["small_configs"] = gpu_small_configs(args, ceil)
     if not args.no_layer:
         line["swiglu_layer"] = gpu_swiglu_layer(args)
-    if args.copy_calibration:
+    if args.copy_calibration or args.counter_pass:
         copy_calibration()
+    if args.counter_pass:
+        print(json.dumps({"counter_pass": {"labels": COUNTER["labels"], "reps": COUNTER_REPS,
+                                           "algorithmic_bytes": COUNTER["alg"]}}), flush=True)
+        return
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(args, c)
     print(json.dumps(line), flush=True)
