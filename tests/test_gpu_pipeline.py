@@ -196,19 +196,22 @@ def grade_tile(name, got, aq, as_, bq, bs, is_bf16, g):
     return res
 
 
-def test_expert_step_whole_tiles(case):
-    """Whole output tiles of the large workload's GEMMs, as the benchmark runs
-    them (bf16 outputs), against the oracle on the kernel's own MX operand
-    bytes: for fwd and dgrad the last, partly filled 256-row tile of three
+@pytest.mark.parametrize("out_dtype", [MX_OUT_BF16, MX_OUT_F32])
+def test_expert_step_whole_tiles(case, out_dtype):
+    """Whole output tiles of the large workload's GEMMs, with bf16 outputs as
+    the benchmark runs them and with fp32 outputs (the accumulation error
+    without the bf16 rounding over it), against the oracle on the kernel's
+    own MX operand bytes: for fwd and dgrad the last, partly filled 256-row tile of three
     groups (the smallest, the largest, and one next to the empty expert) over
     the first and last 256 output columns; for wgrad a full 256 x 256 dW tile
     of three groups whose rows start inside a 128-row scale panel."""
     c, x, w, ids, dy, dy_np, (counts, off, dst, src) = case
     T, K, N, E, topk, cap = c["T"], c["K"], c["N"], c["E"], c["topk"], c["capacity"]
-    b = moe.ExpertBuffers(T, K, N, E, topk, out_dtype=MX_OUT_BF16)
+    b = moe.ExpertBuffers(T, K, N, E, topk, out_dtype=out_dtype)
     moe.expert_step(b, x, w, dy, ids)
     torch.cuda.synchronize()
     g = np.random.default_rng(77)
+    is_bf16 = out_dtype == MX_OUT_BF16
     live = [e for e in range(E) if counts[e] > 0]
     empty = [e for e in range(E) if counts[e] == 0]
     nxt = [e for e in live if abs(e - empty[0]) == 1]
@@ -229,10 +232,10 @@ def test_expert_step_whole_tiles(case):
         assert np.array_equal(dyq[rows], oq) and np.array_equal(dys[rows], os_)
         for cols in (np.arange(0, 256), np.arange(N - 256, N)):
             grade_tile(f"fwd e={e} rows {r0}:{hi} cols {cols[0]}", y[np.ix_(rows, cols)], xpq[rows], xps[rows],
-                       wq[e][cols], ws[e * N + cols], True, g)
+                       wq[e][cols], ws[e * N + cols], is_bf16, g)
         for cols in (np.arange(0, 256), np.arange(K - 256, K)):
             grade_tile(f"dgrad e={e} rows {r0}:{hi} cols {cols[0]}", dx[np.ix_(rows, cols)], dyq[rows], dys[rows],
-                       wtq[e][cols], wts[e * K + cols], True, g)
+                       wtq[e][cols], wts[e * K + cols], is_bf16, g)
     # wgrad: groups whose rows start inside a 128-row panel
     dytq, dyts = host(b.dytq), srows(b.dyts, cap)
     xtq, xts = host(b.xtq), srows(b.xts, cap)
@@ -252,4 +255,4 @@ def test_expert_step_whole_tiles(case):
         cq, cs = mx.quantize_rowwise(np.ascontiguousarray(dy_np[lo:hi, n0:n0 + 256].T))
         assert np.array_equal(dytq[nr, lo:hi], cq) and np.array_equal(dyts[nr, lo // 32:hi // 32], cs)
         grade_tile(f"wgrad e={e} rows {lo}:{hi} tile ({n0},{k0})", dw[e][np.ix_(nr, kr)], aq,
-                   dyts[nr, kb // 32:hi // 32], bq, xts[kr, kb // 32:hi // 32], True, g)
+                   dyts[nr, kb // 32:hi // 32], bq, xts[kr, kb // 32:hi // 32], is_bf16, g)
