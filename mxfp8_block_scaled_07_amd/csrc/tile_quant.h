@@ -23,10 +23,13 @@
 //   writes 8 columns x 16 bytes into an LDS tile kept column-major (a column
 //   = 128 rows = 256 bytes = 16 slots of 16 bytes; slot s of column c sits
 //   at slot s ^ ((c ^ (c >> 3)) & 15), which keeps both the write and the
-//   read pattern spread over all banks).  Thread (column c, half h) then
-//   reads rows 64h .. 64h+63 of column c, quantizes its two 32-row blocks,
-//   writes 64 contiguous code bytes and the two scale bytes (a 16-bit store;
-//   the 4 scale bytes of a column tile form one panel dword).
+//   read pattern spread over all banks).  Then 8 lanes take a column, 16
+//   rows each: a lane pair shares a 32-row block (amax exchanged with a DPP
+//   quad permute), and the 8 lanes store the column's 128 code bytes as one
+//   whole line, so a wave's store writes 8 whole lines (lanes holding 64
+//   bytes of two 32-row blocks each wrote 16-byte pieces of 32 lines per
+//   store, 4-15% slower).  The column's 4 scale bytes are merged into one
+//   panel dword with DPP row shifts.
 #pragma once
 
 #include "mx_device.h"
@@ -175,38 +178,45 @@ __global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const 
       *reinterpret_cast<uint4*>(lds + cc * 256 + 16 * (slot ^ tq_swz(cc))) = make_uint4(d[0], d[1], d[2], d[3]);
     }
     __syncthreads();
-    const int c = t >> 1, hf = t & 1;
-    const int64_t gc = c0 + c;
-    if (gc < sh.cols) {
-      uint32_t sbs = 0;
+    // 8 lanes per column, 16 rows each (two slots): the 8 lanes of a column
+    // store its 128 code bytes as one whole line.  Lanes 2q and 2q + 1 share
+    // the 32-row block q (amax exchanged with a DPP quad permute); the
+    // column's 4 scale bytes (lanes 0, 2, 4, 6 of the group) are merged with
+    // row shifts into lane 6, which stores the panel dword.
+    const int p = t & 7;
+    const int64_t C = (int64_t)sh.batch * sh.cols;
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        uint4 q4[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          q4[s] = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((8 * hf + 4 * blk + s) ^ tq_swz(c)));
-        uint32_t m = 0;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t ms = amax8(q4[s]);
-          m = m > ms ? m : ms;
-        }
-        const uint32_t sb = scale_byte_from_amax(m);
-        const float sc = e8m0_to_f32(sb);
-        sbs |= sb << (8 * blk);
-        const int64_t gr = r0 + 64 * hf + 32 * blk;
-        if (gr < sh.rows_out) {
-          uint8_t* dst = o.col_q + ((int64_t)b * sh.cols + gc) * sh.rows_out + gr;
-          *reinterpret_cast<uint4*>(dst) = make_uint4(cvt4_e4m3(q4[0].x, q4[0].y, sc), cvt4_e4m3(q4[0].z, q4[0].w, sc),
-                                                      cvt4_e4m3(q4[1].x, q4[1].y, sc), cvt4_e4m3(q4[1].z, q4[1].w, sc));
-          *reinterpret_cast<uint4*>(dst + 16) =
-              make_uint4(cvt4_e4m3(q4[2].x, q4[2].y, sc), cvt4_e4m3(q4[2].z, q4[2].w, sc),
-                         cvt4_e4m3(q4[3].x, q4[3].y, sc), cvt4_e4m3(q4[3].z, q4[3].w, sc));
-        }
+    for (int it = 0; it < 4; ++it) {
+      const int c = 32 * it + (t >> 3);
+      const int64_t gc = c0 + c;
+      const uint4 q0 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p) ^ tq_swz(c)));
+      const uint4 q1 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p + 1) ^ tq_swz(c)));
+      const uint32_t m0 = amax8(q0), m1 = amax8(q1);
+      uint32_t m = m0 > m1 ? m0 : m1;
+      const uint32_t mo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+      m = m > mo ? m : mo;
+      const uint32_t sb = scale_byte_from_amax(m);
+      const float sc = e8m0_to_f32(sb);
+      const int64_t gr = r0 + 16 * p;   // rows_out % 32 == 0: the 16 rows are all in or all out
+      if (gc < sh.cols && gr < sh.rows_out) {
+        typedef unsigned int v4u_ __attribute__((ext_vector_type(4)));
+        const v4u_ cw = {cvt4_e4m3(q0.x, q0.y, sc), cvt4_e4m3(q0.z, q0.w, sc), cvt4_e4m3(q1.x, q1.y, sc),
+                         cvt4_e4m3(q1.z, q1.w, sc)};
+        v4u_* dst = reinterpret_cast<v4u_*>(o.col_q + ((int64_t)b * sh.cols + gc) * sh.rows_out + gr);
+        // Gathered sources walk the row bands of a column tile, so their
+        // columnwise lines are written front to back: streamed (non-temporal)
+        // stores are faster there (measured 7% on the gathered columnwise
+        // quantize) and slightly slower for the plain order.
+        if constexpr (Src::kGathered) __builtin_nontemporal_store(cw, dst);
+        else *dst = cw;
       }
-      const int64_t C = (int64_t)sh.batch * sh.cols;
-      *reinterpret_cast<uint16_t*>(o.col_s + ((r0 >> 7) * C + (int64_t)b * sh.cols + gc) * 4 + 2 * hf) =
-          (uint16_t)sbs;
+      uint32_t d = (p & 1) ? 0u : sb << (8 * (p >> 1));
+      const uint32_t d2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x112, 0xF, 0xF, true);  // lane - 2
+      d |= p >= 2 ? d2 : 0u;
+      const uint32_t d4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x114, 0xF, 0xF, true);  // lane - 4
+      d |= p >= 4 ? d4 : 0u;
+      if (p == 6 && gc < sh.cols)
+        *reinterpret_cast<uint32_t*>(o.col_s + ((r0 >> 7) * C + (int64_t)b * sh.cols + gc) * 4) = d;
     }
   }
 }
