@@ -50,6 +50,8 @@ struct SrcSwiglu {
   struct Table {};
   static constexpr bool kTable = false;
   static constexpr bool kGathered = false;
+  static constexpr int kSub = 1;
+  static constexpr bool kFetchAll = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -64,7 +66,7 @@ struct SrcSwiglu {
   struct Raw {
     uint4 g, u;
   };
-  __device__ Raw fetch(const Row& w, int64_t col) const {
+  __device__ Raw fetch(const Row& w, int64_t col, bool) const {
     Raw x;
     x.g = *reinterpret_cast<const uint4*>(w.p + col);
     x.u = *reinterpret_cast<const uint4*>(w.p + F + col);
@@ -91,6 +93,8 @@ struct SrcSwigluBwd {
   struct Table {};
   static constexpr bool kTable = false;
   static constexpr bool kGathered = false;
+  static constexpr int kSub = 1;
+  static constexpr bool kFetchAll = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -107,7 +111,7 @@ struct SrcSwigluBwd {
   struct Raw {
     uint4 g, u, d;
   };
-  __device__ Raw fetch(const Row& w, int64_t col) const {
+  __device__ Raw fetch(const Row& w, int64_t col, bool) const {
     const bool gate = col < F;  // du needs no u
     const int64_t c = gate ? col : col - F;
     Raw x;
@@ -150,12 +154,14 @@ struct SrcCombineBwd {
   int64_t tokens;
   int32_t topk;
   int64_t cols;
+  bool vec;   // topk is 4 or 8, dst_row and weights 16-byte aligned: a token's slots load as vectors
   struct Table {
     int32_t tok[kTq];
     float w[kTq];
   };
   static constexpr bool kTable = true;
   static constexpr bool kGathered = true;
+  static constexpr int kSub = 4;   // the pair table is built once for 4 column tiles
   __device__ void fill_table(Table& tb, int64_t, int64_t r0, int64_t rows_out) const {
     const int t = threadIdx.x;
     if (t < kTq) {
@@ -165,33 +171,61 @@ struct SrcCombineBwd {
       if (r < rows_out) {
         const int32_t s = src_row[r];
         if (s >= 0 && s < tokens) {
-          for (int32_t j = 0; j < topk; ++j)
-            if (dst_row[(int64_t)s * topk + j] == r) {
-              tok = s;
-              w = weights[(int64_t)s * topk + j];
-              break;
+          const int64_t p0 = (int64_t)s * topk;
+          if (vec) {
+            // the token's slots and weights are contiguous and 16-byte
+            // aligned: loaded together as 16-byte vectors, in one round trip
+            // instead of a chain of dependent loads
+            const int4* d4 = reinterpret_cast<const int4*>(dst_row + p0);
+            const float4* w4 = reinterpret_cast<const float4*>(weights + p0);
+#pragma unroll
+            for (int q = 1; q >= 0; --q) {   // the smallest matching slot wins
+              if (q == 1 && topk == 4) continue;
+              const int4 d = d4[q];
+              const float4 wq = w4[q];
+              if (d.w == r) { tok = s; w = wq.w; }
+              if (d.z == r) { tok = s; w = wq.z; }
+              if (d.y == r) { tok = s; w = wq.y; }
+              if (d.x == r) { tok = s; w = wq.x; }
             }
+          } else {
+            for (int32_t j = 0; j < topk; ++j)
+              if (dst_row[p0 + j] == r) {
+                tok = s;
+                w = weights[p0 + j];
+                break;
+              }
+          }
         }
       }
       tb.tok[t] = tok;
       tb.w[t] = w;
     }
   }
+  // kept for several column tiles: the token index, not a 64-bit pointer
   struct Row {
     bool ok;
-    const uint16_t* p;
+    int32_t tok;
     float w;
   };
   __device__ Row row(const Table& tb, int64_t, int64_t, int lr, bool in_range) const {
-    const int32_t tok = tb.tok[lr];
     Row x;
-    x.ok = in_range && tok >= 0;
-    x.p = dout + (int64_t)tok * cols;
+    x.tok = tb.tok[lr];
+    x.ok = in_range && x.tok >= 0;
     x.w = tb.w[lr];
     return x;
   }
   typedef uint4 Raw;
-  __device__ Raw fetch(const Row& x, int64_t col) const { return *reinterpret_cast<const uint4*>(x.p + col); }
+  // Called for every row, valid or not (no divergent loads in the column-tile
+  // loop): invalid rows read token 0's row, a chunk past the last column
+  // reads column 0, and the tile code discards both.  Without tokens, dout
+  // may be null and nothing is read.
+  static constexpr bool kFetchAll = true;
+  __device__ Raw fetch(const Row& x, int64_t col, bool col_ok) const {
+    if (tokens == 0) return make_uint4(0, 0, 0, 0);
+    const int64_t t = x.ok ? x.tok : 0;
+    return *reinterpret_cast<const uint4*>(dout + t * cols + (col_ok ? col : 0));
+  }
   __device__ uint4 finish(const Raw& v, const Row& x, int64_t) const {
     uint4 o;
     o.x = bf16x2_rne(x.w * bf_lo(v.x), x.w * bf_hi(v.x));
@@ -323,6 +357,7 @@ extern "C" int mx_combine_bwd_quantize(const uint16_t* dout, const float* weight
   TqShape sh;
   unsigned grid;
   if (!tq_shape(1, rows, H, sh, grid)) return MX_EINVAL;
-  return tq_launch(SrcCombineBwd{dout, weights, dst_row, src_row, tokens, topk, H}, sh, grid,
+  const bool vec = (topk == 4 || topk == 8) && !misaligned(dst_row, 16) && !misaligned(weights, 16);
+  return tq_launch(SrcCombineBwd{dout, weights, dst_row, src_row, tokens, topk, H, vec}, sh, grid,
                    TqOut{row_q, row_s, col_q, col_s, dy}, reinterpret_cast<hipStream_t>(stream));
 }

@@ -26,6 +26,8 @@ struct SrcPlain {
   struct Table {};
   static constexpr bool kTable = false;
   static constexpr bool kGathered = false;
+  static constexpr int kSub = 1;
+  static constexpr bool kFetchAll = false;
   __device__ void fill_table(Table&, int64_t, int64_t, int64_t) const {}
   struct Row {
     bool ok;
@@ -38,7 +40,7 @@ struct SrcPlain {
     return w;
   }
   typedef uint4 Raw;
-  __device__ Raw fetch(const Row& w, int64_t col) const { return *reinterpret_cast<const uint4*>(w.p + col); }
+  __device__ Raw fetch(const Row& w, int64_t col, bool) const { return *reinterpret_cast<const uint4*>(w.p + col); }
   __device__ uint4 finish(const Raw& v, const Row&, int64_t) const { return v; }
 };
 
@@ -51,6 +53,8 @@ struct SrcGather {
   };
   static constexpr bool kTable = true;
   static constexpr bool kGathered = true;
+  static constexpr int kSub = 1;
+  static constexpr bool kFetchAll = false;
   __device__ void fill_table(Table& tb, int64_t, int64_t r0, int64_t rows_out) const {
     const int t = threadIdx.x;
     if (t < kTq) {
@@ -75,7 +79,7 @@ struct SrcGather {
     return w;
   }
   typedef uint4 Raw;
-  __device__ Raw fetch(const Row& w, int64_t col) const { return *reinterpret_cast<const uint4*>(w.p + col); }
+  __device__ Raw fetch(const Row& w, int64_t col, bool) const { return *reinterpret_cast<const uint4*>(w.p + col); }
   __device__ uint4 finish(const Raw& v, const Row&, int64_t) const { return v; }
 };
 

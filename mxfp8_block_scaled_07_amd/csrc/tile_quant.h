@@ -79,7 +79,10 @@ __device__ __forceinline__ uint32_t amax8(const uint4& v) {
 //   struct Row { bool ok; ... };
 //   __device__ Row row(const Table&, int64_t b, int64_t r, int local_r, bool in_range) const;
 //   struct Raw;
-//   __device__ Raw fetch(const Row&, int64_t col) const;     only when row.ok
+//   __device__ Raw fetch(const Row&, int64_t col, bool col_ok) const;  only for row.ok && col_ok
+//     unless kFetchAll (then for every row, and it must stay in bounds)
+//   static constexpr int kSub;             column tiles per workgroup
+//   static constexpr bool kFetchAll;
 //   __device__ uint4 finish(const Raw&, const Row&, int64_t col) const;   8 bf16
 // Rows or columns outside the output, and rows the source marks !ok, are
 // zero: they raise no amax and produce zero codes (and zero pad scales).
@@ -92,131 +95,149 @@ __device__ __forceinline__ uint32_t amax8(const uint4& v) {
 // MB) and hit in the caches instead of HBM.
 template <class Src, bool kRow, bool kCol, bool kY>
 __global__ void __launch_bounds__(kTqThreads) k_tile_quant(const Src src, const TqShape sh, const TqOut o) {
-  // The source's row table is only read while the tile is loaded, before the
-  // column phase writes the LDS tile: it shares the tile's first bytes, so a
-  // gathered tile needs no more LDS than a plain one (5 workgroups per CU).
+  // The source's row table is only read before the first column phase writes
+  // the LDS tile: it shares the tile's first bytes, so a gathered tile needs
+  // no more LDS than a plain one (5 workgroups per CU).
   typedef typename Src::Table Table;
   constexpr int kTile = kCol ? kTq * kTq * 2 : 16;
   constexpr int kLds = kTile > (int)sizeof(Table) ? kTile : (int)sizeof(Table);
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];
   Table& table = *reinterpret_cast<Table*>(lds);
+  // A workgroup takes kSub consecutive column tiles of one row band: the
+  // source's row table and the threads' row descriptors are built once.
+  constexpr int kSub = Src::kSub;
+  const uint32_t n_tcg = ((uint32_t)sh.n_tc + kSub - 1) / kSub;
   uint32_t idx = blockIdx.x;
-  int32_t tc, tr;
+  int32_t tcg, tr;
   if (Src::kGathered) {
     tr = (int32_t)(idx % (uint32_t)sh.n_tr);
     idx /= (uint32_t)sh.n_tr;
-    tc = (int32_t)(idx % (uint32_t)sh.n_tc);
-    idx /= (uint32_t)sh.n_tc;
+    tcg = (int32_t)(idx % n_tcg);
+    idx /= n_tcg;
   } else {
-    tc = (int32_t)(idx % (uint32_t)sh.n_tc);
-    idx /= (uint32_t)sh.n_tc;
+    tcg = (int32_t)(idx % n_tcg);
+    idx /= n_tcg;
     tr = (int32_t)(idx % (uint32_t)sh.n_tr);
     idx /= (uint32_t)sh.n_tr;
   }
   const int32_t b = (int32_t)idx;
-  const int64_t r0 = (int64_t)tr * kTq, c0 = (int64_t)tc * kTq;
+  const int64_t r0 = (int64_t)tr * kTq;
   const int t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int ch = lane & 15, ry = lane >> 4;
   const int lr0 = 32 * w + 8 * ry;
-  const int64_t col = c0 + 8 * ch;
-  const bool col_ok = col < sh.cols;  // cols % 32 == 0: a chunk is all in or all out
   if (Src::kTable) {
     src.fill_table(table, b, r0, sh.rows_out);
     __syncthreads();
   }
-
-  uint4 v[8];
-  {
-    typename Src::Row rw[8];
-    typename Src::Raw raw[8];
+  typename Src::Row rw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + lr0 + i;
-      rw[i] = src.row(table, b, r, lr0 + i, r < sh.rows_out && col_ok);
-      if (rw[i].ok) raw[i] = src.fetch(rw[i], col);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = rw[i].ok ? src.finish(raw[i], rw[i], col) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r0 + lr0 + i;
+    rw[i] = src.row(table, b, r, lr0 + i, r < sh.rows_out);
   }
 
-  if (kRow || kY) {
-    const int64_t R = (int64_t)sh.batch * sh.rows_out;
+#pragma unroll 1
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int32_t tc = tcg * kSub + sub;
+    if (tc >= sh.n_tc) break;   // uniform over the workgroup
+    const int64_t c0 = (int64_t)tc * kTq;
+    const int64_t col = c0 + 8 * ch;
+    const bool col_ok = col < sh.cols;  // cols % 32 == 0: a chunk is all in or all out
+
+    uint4 v[8];
+    {
+      typename Src::Raw raw[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r0 + lr0 + i;
-      const bool r_ok = r < sh.rows_out;
-      const int64_t orow = (int64_t)b * sh.rows_out + r;
-      if (kY && r_ok && col_ok) *reinterpret_cast<uint4*>(o.y + orow * sh.cols + col) = v[i];
-      if (kRow) {
-        const uint32_t sb = scale_byte_from_amax(quad_max(amax8(v[i])));
+      for (int i = 0; i < 8; ++i) {
+        if constexpr (Src::kFetchAll) raw[i] = src.fetch(rw[i], col, col_ok);
+        else if (rw[i].ok && col_ok) raw[i] = src.fetch(rw[i], col, true);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        v[i] = rw[i].ok && col_ok ? src.finish(raw[i], rw[i], col) : make_uint4(0, 0, 0, 0);
+    }
+
+    if (kRow || kY) {
+      const int64_t R = (int64_t)sh.batch * sh.rows_out;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + lr0 + i;
+        const bool r_ok = r < sh.rows_out;
+        const int64_t orow = (int64_t)b * sh.rows_out + r;
+        if (kY && r_ok && col_ok) *reinterpret_cast<uint4*>(o.y + orow * sh.cols + col) = v[i];
+        if (kRow) {
+          const uint32_t sb = scale_byte_from_amax(quad_max(amax8(v[i])));
+          const float sc = e8m0_to_f32(sb);
+          if (r_ok && col_ok)
+            *reinterpret_cast<uint2*>(o.row_q + orow * sh.cols + col) =
+                make_uint2(cvt4_e4m3(v[i].x, v[i].y, sc), cvt4_e4m3(v[i].z, v[i].w, sc));
+          uint32_t d = sb << (8 * (ch >> 2));
+          d |= dpp_row_shr(d, 4);
+          d |= dpp_row_shr(d, 8);
+          if (r_ok && ch == 12) *reinterpret_cast<uint32_t*>(o.row_s + ((c0 >> 7) * R + orow) * 4) = d;
+        }
+      }
+    }
+
+    if (kCol) {
+      // every wave is done with the row table (it shares the LDS tile) and with
+      // the previous column tile's reads
+      if (Src::kTable || kSub > 1) __syncthreads();
+      const int slot = lr0 >> 3;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int cc = 8 * ch + j;
+        const int k = j >> 1;
+        uint32_t d[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t a = tq_comp(v[2 * p], k), bb = tq_comp(v[2 * p + 1], k);
+          d[p] = (j & 1) ? (a >> 16) | (bb & 0xFFFF0000u) : (a & 0xFFFFu) | (bb << 16);
+        }
+        *reinterpret_cast<uint4*>(lds + cc * 256 + 16 * (slot ^ tq_swz(cc))) = make_uint4(d[0], d[1], d[2], d[3]);
+      }
+      __syncthreads();
+      // 8 lanes per column, 16 rows each (two slots): the 8 lanes of a column
+      // store its 128 code bytes as one whole line.  Lanes 2q and 2q + 1 share
+      // the 32-row block q (amax exchanged with a DPP quad permute); the
+      // column's 4 scale bytes (lanes 0, 2, 4, 6 of the group) are merged with
+      // row shifts into lane 6, which stores the panel dword.
+      const int p = t & 7;
+      const int64_t C = (int64_t)sh.batch * sh.cols;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int c = 32 * it + (t >> 3);
+        const int64_t gc = c0 + c;
+        const uint4 q0 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p) ^ tq_swz(c)));
+        const uint4 q1 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p + 1) ^ tq_swz(c)));
+        const uint32_t m0 = amax8(q0), m1 = amax8(q1);
+        uint32_t m = m0 > m1 ? m0 : m1;
+        const uint32_t mo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+        m = m > mo ? m : mo;
+        const uint32_t sb = scale_byte_from_amax(m);
         const float sc = e8m0_to_f32(sb);
-        if (r_ok && col_ok)
-          *reinterpret_cast<uint2*>(o.row_q + orow * sh.cols + col) =
-              make_uint2(cvt4_e4m3(v[i].x, v[i].y, sc), cvt4_e4m3(v[i].z, v[i].w, sc));
-        uint32_t d = sb << (8 * (ch >> 2));
-        d |= dpp_row_shr(d, 4);
-        d |= dpp_row_shr(d, 8);
-        if (r_ok && ch == 12) *reinterpret_cast<uint32_t*>(o.row_s + ((c0 >> 7) * R + orow) * 4) = d;
+        const int64_t gr = r0 + 16 * p;   // rows_out % 32 == 0: the 16 rows are all in or all out
+        if (gc < sh.cols && gr < sh.rows_out) {
+          typedef unsigned int v4u_ __attribute__((ext_vector_type(4)));
+          const v4u_ cw = {cvt4_e4m3(q0.x, q0.y, sc), cvt4_e4m3(q0.z, q0.w, sc), cvt4_e4m3(q1.x, q1.y, sc),
+                           cvt4_e4m3(q1.z, q1.w, sc)};
+          v4u_* dst = reinterpret_cast<v4u_*>(o.col_q + ((int64_t)b * sh.cols + gc) * sh.rows_out + gr);
+          // Gathered sources walk the row bands of a column tile, so their
+          // columnwise lines are written front to back: streamed (non-temporal)
+          // stores are faster there (measured 7% on the gathered columnwise
+          // quantize) and slightly slower for the plain order.
+          if constexpr (Src::kGathered) __builtin_nontemporal_store(cw, dst);
+          else *dst = cw;
+        }
+        uint32_t d = (p & 1) ? 0u : sb << (8 * (p >> 1));
+        const uint32_t d2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x112, 0xF, 0xF, true);  // lane - 2
+        d |= p >= 2 ? d2 : 0u;
+        const uint32_t d4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x114, 0xF, 0xF, true);  // lane - 4
+        d |= p >= 4 ? d4 : 0u;
+        if (p == 6 && gc < sh.cols)
+          *reinterpret_cast<uint32_t*>(o.col_s + ((r0 >> 7) * C + (int64_t)b * sh.cols + gc) * 4) = d;
       }
-    }
-  }
-
-  if (kCol) {
-    if (Src::kTable) __syncthreads();  // every wave is done with the row table (it shares the LDS tile)
-    const int slot = lr0 >> 3;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int cc = 8 * ch + j;
-      const int k = j >> 1;
-      uint32_t d[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t a = tq_comp(v[2 * p], k), bb = tq_comp(v[2 * p + 1], k);
-        d[p] = (j & 1) ? (a >> 16) | (bb & 0xFFFF0000u) : (a & 0xFFFFu) | (bb << 16);
-      }
-      *reinterpret_cast<uint4*>(lds + cc * 256 + 16 * (slot ^ tq_swz(cc))) = make_uint4(d[0], d[1], d[2], d[3]);
-    }
-    __syncthreads();
-    // 8 lanes per column, 16 rows each (two slots): the 8 lanes of a column
-    // store its 128 code bytes as one whole line.  Lanes 2q and 2q + 1 share
-    // the 32-row block q (amax exchanged with a DPP quad permute); the
-    // column's 4 scale bytes (lanes 0, 2, 4, 6 of the group) are merged with
-    // row shifts into lane 6, which stores the panel dword.
-    const int p = t & 7;
-    const int64_t C = (int64_t)sh.batch * sh.cols;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int c = 32 * it + (t >> 3);
-      const int64_t gc = c0 + c;
-      const uint4 q0 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p) ^ tq_swz(c)));
-      const uint4 q1 = *reinterpret_cast<const uint4*>(lds + c * 256 + 16 * ((2 * p + 1) ^ tq_swz(c)));
-      const uint32_t m0 = amax8(q0), m1 = amax8(q1);
-      uint32_t m = m0 > m1 ? m0 : m1;
-      const uint32_t mo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-      m = m > mo ? m : mo;
-      const uint32_t sb = scale_byte_from_amax(m);
-      const float sc = e8m0_to_f32(sb);
-      const int64_t gr = r0 + 16 * p;   // rows_out % 32 == 0: the 16 rows are all in or all out
-      if (gc < sh.cols && gr < sh.rows_out) {
-        typedef unsigned int v4u_ __attribute__((ext_vector_type(4)));
-        const v4u_ cw = {cvt4_e4m3(q0.x, q0.y, sc), cvt4_e4m3(q0.z, q0.w, sc), cvt4_e4m3(q1.x, q1.y, sc),
-                         cvt4_e4m3(q1.z, q1.w, sc)};
-        v4u_* dst = reinterpret_cast<v4u_*>(o.col_q + ((int64_t)b * sh.cols + gc) * sh.rows_out + gr);
-        // Gathered sources walk the row bands of a column tile, so their
-        // columnwise lines are written front to back: streamed (non-temporal)
-        // stores are faster there (measured 7% on the gathered columnwise
-        // quantize) and slightly slower for the plain order.
-        if constexpr (Src::kGathered) __builtin_nontemporal_store(cw, dst);
-        else *dst = cw;
-      }
-      uint32_t d = (p & 1) ? 0u : sb << (8 * (p >> 1));
-      const uint32_t d2 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x112, 0xF, 0xF, true);  // lane - 2
-      d |= p >= 2 ? d2 : 0u;
-      const uint32_t d4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)d, 0x114, 0xF, 0xF, true);  // lane - 4
-      d |= p >= 4 ? d4 : 0u;
-      if (p == 6 && gc < sh.cols)
-        *reinterpret_cast<uint32_t*>(o.col_s + ((r0 >> 7) * C + (int64_t)b * sh.cols + gc) * 4) = d;
     }
   }
 }
@@ -240,7 +261,10 @@ inline bool tq_shape(int64_t batch, int64_t rows_out, int64_t cols, TqShape& sh,
 template <class Src>
 inline int tq_launch(const Src& src, const TqShape& sh, unsigned grid, const TqOut& o, hipStream_t st) {
   const bool r = o.row_q != nullptr, c = o.col_q != nullptr, y = o.y != nullptr;
-  const dim3 g(grid), bl(kTqThreads);
+  // grid: tiles, or groups of Src::kSub column tiles
+  const dim3 g(Src::kSub == 1 ? grid
+                              : (unsigned)((int64_t)sh.batch * sh.n_tr * ((sh.n_tc + Src::kSub - 1) / Src::kSub))),
+      bl(kTqThreads);
   if (r && c && y) hipLaunchKernelGGL((k_tile_quant<Src, true, true, true>), g, bl, 0, st, src, sh, o);
   else if (r && c) hipLaunchKernelGGL((k_tile_quant<Src, true, true, false>), g, bl, 0, st, src, sh, o);
   else if (r && y) hipLaunchKernelGGL((k_tile_quant<Src, true, false, true>), g, bl, 0, st, src, sh, o);
