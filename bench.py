@@ -714,32 +714,11 @@ def summarize_counters(fetch_csv, write_csv, log, out_path=TRAFFIC_FILE):
     names; a stage's bytes are the mean over its calls of the summed counter
     (KiB) of its dispatches, scaled by what the same counter reads for a plain
     copy of CALIB_BYTES."""
-    import csv
-    import statistics
-
     info = [json.loads(ln) for ln in open(log) if ln.startswith('{"counter_pass"')][-1]["counter_pass"]
     labels, alg = info["labels"], info["algorithmic_bytes"]
 
-    def per_label(path):
-        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
-        calls, cur, n_mark = {}, None, 0
-        for r in rows:
-            if MARKER_KERNEL in r["Kernel_Name"]:
-                if n_mark == len(labels):
-                    raise SystemExit(f"{path}: more marker dispatches than the {len(labels)} labels")
-                if cur is not None:
-                    calls.setdefault(cur[0], []).append(cur[1])
-                cur = [labels[n_mark], 0.0]
-                n_mark += 1
-            elif cur is not None:
-                cur[1] += float(r["Counter_Value"])
-        if cur is not None:
-            calls.setdefault(cur[0], []).append(cur[1])
-        if n_mark != len(labels):
-            raise SystemExit(f"{path}: {n_mark} marker dispatches for {len(labels)} labels")
-        return {k: statistics.fmean(v) for k, v in calls.items()}
-
-    f, w = per_label(fetch_csv), per_label(write_csv)
+    f = {lab: d["FETCH_SIZE"] for lab, d in counter_means(fetch_csv, labels).items() if "FETCH_SIZE" in d}
+    w = {lab: d["WRITE_SIZE"] for lab, d in counter_means(write_csv, labels).items() if "WRITE_SIZE" in d}
     ff, fw = CALIB_BYTES / (f["calibration"] * 1024), CALIB_BYTES / (w["calibration"] * 1024)
     cmd = ("cd /tmp && export TMPDIR=/tmp && timeout -s KILL 900 rocprofv3 --pmc {C} -d $GRAFT_REPO_ROOT/gpurun_out/"
            "pmc_{c} -o run --output-format csv -- python3 $GRAFT_REPO_ROOT/bench.py --counter-pass "
@@ -780,6 +759,97 @@ def summarize_counters(fetch_csv, write_csv, log, out_path=TRAFFIC_FILE):
     print(f"wrote {out_path}: {len(out)} lines")
 
 
+GEMM_COUNTER_STAGES = ("gemm_fwd", "gemm_dgrad", "gemm_wgrad", "bf16.gemm_fwd", "bf16.gemm_dgrad", "bf16.gemm_wgrad")
+GEMM_COUNTER_SETS = (
+    "SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VMEM SQ_VMEM_TA_ADDR_FIFO_FULL "
+    "SQ_VMEM_TA_CMD_FIFO_FULL SQ_LDS_BANK_CONFLICT TA_BUSY_avr TA_ADDR_STALLED_BY_TC_CYCLES_sum GRBM_GUI_ACTIVE",
+    "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum TCC_TAG_STALL_sum TCP_TCR_TCP_STALL_CYCLES_sum "
+    "TCP_PENDING_STALL_CYCLES_sum TCP_UTCL1_TRANSLATION_MISS_sum TCP_UTCL1_TRANSLATION_HIT_sum TD_TD_BUSY_sum "
+    "TD_TC_STALL_sum GRBM_GUI_ACTIVE")
+
+
+def counter_means(path, labels):
+    """{label: {counter: mean over the label's calls of the counter summed over the call's dispatches}} from
+    a --pmc CSV of a counter pass (marker kernels delimit the calls)."""
+    import csv
+    import statistics
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: (int(r["Dispatch_Id"]), r["Counter_Name"]))
+    calls, cur, n_mark, last = {}, None, 0, None
+    for r in rows:
+        if MARKER_KERNEL in r["Kernel_Name"]:
+            if r["Dispatch_Id"] == last:
+                continue
+            last = r["Dispatch_Id"]
+            if n_mark == len(labels):
+                raise SystemExit(f"{path}: more marker dispatches than the {len(labels)} labels")
+            if cur is not None:
+                for k, v in cur[1].items():
+                    calls.setdefault(cur[0], {}).setdefault(k, []).append(v)
+            cur = (labels[n_mark], {})
+            n_mark += 1
+        elif cur is not None:
+            cur[1][r["Counter_Name"]] = cur[1].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    if cur is not None:
+        for k, v in cur[1].items():
+            calls.setdefault(cur[0], {}).setdefault(k, []).append(v)
+    if n_mark != len(labels):
+        raise SystemExit(f"{path}: {n_mark} marker dispatches for {len(labels)} labels")
+    return {lab: {k: statistics.fmean(v) for k, v in d.items()} for lab, d in calls.items()}
+
+
+def summarize_gemm_counters(log, csvs, out_path):
+    """Write the GEMM hardware-counter table (profiles/gemm_counters.md) from
+    counter passes of the expert step (one CSV per counter set)."""
+    info = [json.loads(ln) for ln in open(log) if ln.startswith('{"counter_pass"')][-1]["counter_pass"]
+    m = {}
+    for path in csvs:
+        for lab, d in counter_means(path, info["labels"]).items():
+            m.setdefault(lab, {}).update(d)
+    st = GEMM_COUNTER_STAGES
+    names = sorted({k for lab in st for k in m.get(lab, {})})
+    cmd = ("timeout -s KILL 300 rocprofv3 --pmc {C} -d $GRAFT_REPO_ROOT/gpurun_out/gemm_pmc{i} -o run --output-format "
+           "csv -- python3 $GRAFT_REPO_ROOT/bench.py --counter-pass --no-layer --no-quant-bench "
+           "> $GRAFT_REPO_ROOT/gpurun_out/gemm_pmc{i}.log")
+    out = ["# Hardware counters: grouped GEMMs of the expert step, large workload (T=8192, K=5120, N=8192, E=16, "
+           "top-2), MXFP8 and its BF16 baseline", "",
+           f"Mean counter value per call over the counter pass's {info['reps']} calls of each stage (rocprofv3 sums "
+           "over hardware instances; SQ counts in the units it reports). Calls are delimited by the counter pass's "
+           "marker kernels. Commands (from the repository root on one MI355X; one --pmc pass per counter set), then "
+           "the summary:", "", "```", "cd /tmp && export TMPDIR=/tmp"]
+    out += [cmd.format(C=c, i=i + 1) for i, c in enumerate(GEMM_COUNTER_SETS)]
+    out += ["cd $GRAFT_REPO_ROOT && python3 bench.py --summarize-gemm-counters gpurun_out/gemm_pmc1.log "
+            "gpurun_out/gemm_pmc1/run_counter_collection.csv gpurun_out/gemm_pmc2/run_counter_collection.csv", "```",
+            "", "| counter | " + " | ".join(st) + " |", "|---|" + "---:|" * len(st)]
+    for k in names:
+        out.append(f"| {k} | " + " | ".join(f"{m.get(lab, {}).get(k, float('nan')):.4g}" for lab in st) + " |")
+
+    def der(lab, f):
+        d = m.get(lab, {})
+        try:
+            return f"{f(d):.2f}"
+        except (KeyError, ZeroDivisionError):
+            return "n/a"
+    rows = [("MFMA busy", lambda d: d["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (d["GRBM_GUI_ACTIVE"] / 8)),
+            ("L2 hit rate", lambda d: d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"])),
+            ("TD busy", lambda d: d["TD_TD_BUSY_sum"] / 256 / (d["GRBM_GUI_ACTIVE"] / 8)),
+            ("TD stalled on L1-L2", lambda d: d["TD_TC_STALL_sum"] / 256 / (d["GRBM_GUI_ACTIVE"] / 8))]
+    out += ["", "Derived (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs); TCC_HIT / (TCC_HIT + "
+            "TCC_MISS); TD_TD_BUSY and TD_TC_STALL / 256 CUs / (GRBM_GUI_ACTIVE / 8)):", "",
+            "| | " + " | ".join(st) + " |", "|---|" + "---:|" * len(st)]
+    for name, f in rows:
+        out.append(f"| {name} | " + " | ".join(der(lab, f) for lab in st) + " |")
+    out += ["", "Notes:",
+            "- A bf16 32x32x16 MFMA does a quarter of the work of a scaled FP8 32x32x64 MFMA in half its cycles, so "
+            "the bf16 GEMMs count twice the MFMA busy cycles for the same FLOPs (the 2:1 ratio of the two dense "
+            "peaks).",
+            "- MFMA busy includes the MFMAs of padding rows (the ~1092-row groups fill 5 m-tiles of 256 to 85%) and "
+            "of the wgrad ring's padding steps.",
+            "- Under the counter pass the kernels run serialized, one call at a time; their durations are not the "
+            "bench's.", ""]
+    open(out_path, "w").write("\n".join(out))
+    print(f"wrote {out_path}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -796,9 +866,15 @@ def main():
                          "(rocprofv3 --pmc); prints the stage labels instead of timings")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "LOG"),
                     help="write profiles/hbm_traffic.txt from two counter passes (no GPU needed)")
+    ap.add_argument("--summarize-gemm-counters", nargs="+", metavar="LOG_THEN_CSVS",
+                    help="write profiles/gemm_counters.md from a counter pass's log and its --pmc CSVs")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_gemm_counters:
+        summarize_gemm_counters(args.summarize_gemm_counters[0], args.summarize_gemm_counters[1:],
+                                os.path.join(ROOT, "profiles", "gemm_counters.md"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the expert path has no multi-GPU leg "
