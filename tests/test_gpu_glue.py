@@ -150,7 +150,7 @@ def test_combine_top1_unit_weight_is_exact_unpermute():
 
 @pytest.mark.parametrize("T,H,E,topk,dup", [(300, 96, 6, 2, False), (128, 2048, 16, 8, False),
                                             (77, 544, 4, 3, True), (40, 160, 64, 9, False),
-                                            (50, 96, 128, 64, False)])
+                                            (50, 96, 128, 64, False), (200, 416, 8, 4, True)])
 def test_combine_bwd_quantize(T, H, E, topk, dup):
     g = np.random.default_rng(T + H + topk)
     ids, w, off, dst, src = routed(g, T, E, topk, dup)
@@ -171,6 +171,30 @@ def test_combine_bwd_quantize(T, H, E, topk, dup):
     torch.cuda.synchronize()
     for u, v in ((rq, rq2), (rs, rs2), (cq, cq2), (cs, cs2)):
         assert torch.equal(u, v)
+
+
+def test_combine_bwd_misaligned_metadata_same_bytes():
+    """Top-8 pair lookup with dst_row and weights at 4-byte (not 16-byte)
+    aligned addresses takes the scalar path; the bytes are the same."""
+    g = np.random.default_rng(5)
+    T, H, E, topk = 96, 544, 16, 8
+    ids, w, off, dst, src = routed(g, T, E, topk)
+    rows = src.size
+    dout_np = workloads.normal_bf16(g, (T, H), 1.0, outlier_p=0.01)
+    dout = dev(dout_np)
+    a = mxa.combine_bwd_quantize(dout, dev(w), dev(dst), dev(src), topk, rows, rowwise=True, colwise=True,
+                                 want_bf16=True)
+    dst_m = torch.zeros(dst.size + 1, dtype=torch.int32, device="cuda:0")
+    w_m = torch.zeros(w.size + 1, dtype=torch.float32, device="cuda:0")
+    dst_m[1:] = dev(dst.ravel())
+    w_m[1:] = dev(w.ravel())
+    assert dst_m[1:].data_ptr() % 16 and w_m[1:].data_ptr() % 16
+    b = mxa.combine_bwd_quantize(dout, w_m[1:], dst_m[1:], dev(src), topk, rows, rowwise=True, colwise=True,
+                                 want_bf16=True)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    assert np.array_equal(host(a[0]), glue.combine_bwd(dout_np, dst, w, topk, rows))
 
 
 def test_glue_empty_inputs():
