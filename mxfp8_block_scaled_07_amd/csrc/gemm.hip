@@ -32,6 +32,12 @@
 // than two steps to hide.  Each step runs its first 8 MFMAs, waits for stage
 // s+1 (one barrier per step), and reads the fragments of step s+1 from LDS
 // during its last 8 MFMAs, so a step never starts on an LDS read.
+// A 128-byte line of an operand row holds two k steps.  The loads of an odd
+// step (second halves of lines) run in the reverse order of the even step's,
+// so the lines fetched last for one step are the first the next one asks
+// for and are still in the CU's L1; and since both steps of a 128-wide scale
+// panel use the same panel dword, odd steps load no scales and take the
+// even step's dwords from registers.
 // LDS rows are 64 B with the 16-byte chunks XOR-swizzled by row (conflict
 // free for the fragment reads).  Workgroups are persistent (one per CU) and
 // walk the output tiles of their XCD's share in an order where concurrently
@@ -59,9 +65,11 @@ constexpr int kXcds = 8;
 constexpr int kMaxGroups = 2048;                        // experts per grouped GEMM call
 constexpr uint32_t kOob = 0x80000000u;                  // voffset that reads as zero
 // Vector-memory instructions per wave per stage: 4 + 4 code blocks of 1 KB
-// and one scale dword per lane for A and for B.  kVmemFirst of them are
-// issued before the mid-step wait, the rest after it.
+// and, for even k steps, one scale dword per lane for A and for B (odd steps:
+// kVmemOdd).  kVmemFirst of them are issued before the mid-step wait, the
+// rest after it.
 constexpr int kVmem = 10;
+constexpr int kVmemOdd = 8;
 constexpr int kVmemFirst = 5;
 
 // The bf16 baseline runs the same kernel with bf16 operands: a 64-byte LDS
@@ -381,10 +389,14 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 }
 
 // The loads of the loader's current k step into one LDS stage: 10
-// instructions per wave (A0 B0 A1 B1 A2 B2 A3 B3 sA sB), issued one by one
+// instructions per wave for an even step (A0 B0 A1 B1 A2 B2 A3 B3 sA sB),
+// the 8 code loads in reverse order for an odd one, issued one by one
 // between the MFMAs.  A loader past its last tile issues the same
-// instructions with out-of-range offsets (they read zeros), so every step
-// issues exactly kVmem instructions per wave.
+// instructions with out-of-range offsets (they read zeros), so every even
+// (odd) step issues exactly kVmem (kVmemOdd) instructions per wave.  Every
+// tile starts on ring stage 0 (the ring holds a multiple of 4 steps), so a
+// step's parity is that of its ring stage; for MX operands k_begin is a
+// multiple of 128 bytes, so steps 2j and 2j + 1 cover one scale panel.
 struct LoadPlan {
   v4u aq, bq, as, bs;
   uint32_t v[4];       // code voffsets (out of range where the chunk is outside [k_lo, k_hi))
@@ -415,7 +427,8 @@ __device__ __forceinline__ LoadPlan plan_loads(const Loader& ld, const LaneLoads
   pl.soff = ld.valid ? (uint32_t)k0 : 0u;
   // a step with no valid k (ring padding) reads no scales: its panel offset
   // may lie past the scale tensor
-  const bool kin = ld.valid & (k0 < ld.t.k_hi) & (k0 + BK > ld.t.k_lo);
+  // (scales are loaded by even steps, for both steps of their 128-wide panel)
+  const bool kin = ld.valid & (k0 < ld.t.k_hi) & (k0 + 2 * BK > ld.t.k_lo);
   pl.sa = (kin & (ll.srow < ld.t.rows_a)) ? 4u * (uint32_t)ll.srow : kOob;
   pl.sb = (kin & (ll.srow < ld.t.rows_b)) ? 4u * (uint32_t)ll.srow : kOob;
   pl.pa = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_a : 0u;
@@ -642,7 +655,7 @@ struct Cursor {
 // Vector memory operations complete in issue order, stores included, and
 // every tile store issues exactly tile_stores() instructions per wave.  So
 // the two mid-step waits right after a tile store have at least that many
-// more younger operations behind the loads they wait for (see kVmAfter).
+// more younger operations behind the loads they wait for (see kVmAfterE/O).
 // The epilogue stages through LDS stage 3, which the next step's loads
 // overwrite: a barrier after it keeps every wave's reads ahead of them.
 template <bool kF32, bool kWgrad, bool kBf16>
@@ -715,22 +728,30 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   const uint8_t* nSA = nst + kScaleOff + wm * 128 * 4;
   const uint8_t* nB = nst + kCodeBytes + wn * 128 * BK;
   const uint8_t* nSB = nst + kScaleOff + BM * 4 + wn * 128 * 4;
+  // Steps 2j and 2j + 1 share their panel dwords (raw in cur.sa / cur.sb):
+  // an even step reads them from LDS and hands them on to the odd step, whose
+  // stage holds no scales.  The loads issued here are for step s+3, of the
+  // other parity: an even step issues the odd step's 8 code loads, reversed.
+  constexpr bool kOdd = (CUR & 1) == 1;
+  int xa[4] = {0, 0, 0, 0}, xb[4] = {0, 0, 0, 0};   // the step's scale bytes
   if constexpr (!kBf16) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) cur.sb[j] = scale_byte(cur.sb[j], sel, bok);
-    cur.sa[0] = scale_byte(cur.sa[0], sel, bok);
-    cur.sa[1] = scale_byte(cur.sa[1], sel, bok);
+    for (int j = 0; j < 4; ++j) xb[j] = scale_byte(cur.sb[j], sel, bok);
+    xa[0] = scale_byte(cur.sa[0], sel, bok);
+    xa[1] = scale_byte(cur.sa[1], sel, bok);
   }
   __builtin_amdgcn_sched_barrier(0);
-#define MX_MFMA(i, j) acc[i][j] = mma<kBf16>(cur.b[j], cur.a[i], acc[i][j], cur.sb[j], cur.sa[i]);
+#define MX_MFMA(i, j) acc[i][j] = mma<kBf16>(cur.b[j], cur.a[i], acc[i][j], xb[j], xa[i]);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
-#define MX_SCALE(x) if constexpr (!kBf16) { x; }
+#define MX_LOAD(n) load_n<kBf16>(pl, !kOdd ? 7 - (n) : (n));
+#define MX_SCUR(x) if constexpr (!kBf16 && !kOdd) { x; }
+#define MX_SNXT(x) if constexpr (!kBf16 && kOdd) { x; }
   // first half: MFMAs of A fragments 0, 1; loads 0..4; A fragments 2, 3
-  MX_MFMA(0, 0) load_n<kBf16>(pl, 0); cur.a[2] = frag(A + 64 * BK, fo);                             MX_FENCE
-  MX_MFMA(0, 1) load_n<kBf16>(pl, 1); MX_SCALE(cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc)) MX_FENCE
-  MX_MFMA(0, 2) load_n<kBf16>(pl, 2); cur.a[3] = frag(A + 96 * BK, fo);                             MX_FENCE
-  MX_MFMA(0, 3) load_n<kBf16>(pl, 3); MX_SCALE(cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc)) MX_FENCE
-  MX_MFMA(1, 0) load_n<kBf16>(pl, 4);                                                               MX_FENCE
+  MX_MFMA(0, 0) MX_LOAD(0) cur.a[2] = frag(A + 64 * BK, fo);                             MX_FENCE
+  MX_MFMA(0, 1) MX_LOAD(1) MX_SCUR(cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc)) MX_FENCE
+  MX_MFMA(0, 2) MX_LOAD(2) cur.a[3] = frag(A + 96 * BK, fo);                             MX_FENCE
+  MX_MFMA(0, 3) MX_LOAD(3) MX_SCUR(cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc)) MX_FENCE
+  MX_MFMA(1, 0) MX_LOAD(4)                                                               MX_FENCE
   MX_MFMA(1, 1)                                                                       MX_FENCE
   MX_MFMA(1, 2)                                                                       MX_FENCE
   MX_MFMA(1, 3)                                                                       MX_FENCE
@@ -739,22 +760,31 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
   stage_barrier<kVm>();
   MX_FENCE
   if constexpr (!kBf16) {
-    cur.sa[2] = scale_byte(cur.sa[2], sel, bok);
-    cur.sa[3] = scale_byte(cur.sa[3], sel, bok);
+    xa[2] = scale_byte(cur.sa[2], sel, bok);
+    xa[3] = scale_byte(cur.sa[3], sel, bok);
   }
   // second half: MFMAs of A fragments 2, 3; loads 5..9; the next step's B
   // fragments and A fragments 0, 1
-  MX_MFMA(2, 0) load_n<kBf16>(pl, 5); nxt.b[0] = frag(nB, fo);           MX_SCALE(nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc))       MX_FENCE
-  MX_MFMA(2, 1) load_n<kBf16>(pl, 6); nxt.b[1] = frag(nB + 32 * BK, fo); MX_SCALE(nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc)) MX_FENCE
-  MX_MFMA(2, 2) load_n<kBf16>(pl, 7); nxt.b[2] = frag(nB + 64 * BK, fo); MX_SCALE(nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc)) MX_FENCE
-  MX_MFMA(2, 3) load_n<kBf16>(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo); MX_SCALE(nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc)) MX_FENCE
-  MX_MFMA(3, 0) load_n<kBf16>(pl, 9); nxt.a[0] = frag(nA, fo);           MX_SCALE(nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc))       MX_FENCE
-  MX_MFMA(3, 1)                       nxt.a[1] = frag(nA + 32 * BK, fo); MX_SCALE(nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 0) MX_LOAD(5) nxt.b[0] = frag(nB, fo);           MX_SNXT(nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc))       MX_FENCE
+  MX_MFMA(2, 1) MX_LOAD(6) nxt.b[1] = frag(nB + 32 * BK, fo); MX_SNXT(nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 2) MX_LOAD(7) nxt.b[2] = frag(nB + 64 * BK, fo); MX_SNXT(nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 3) if constexpr (kOdd) load_n<kBf16>(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo); MX_SNXT(nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc)) MX_FENCE
+  MX_MFMA(3, 0) if constexpr (kOdd) load_n<kBf16>(pl, 9); nxt.a[0] = frag(nA, fo);           MX_SNXT(nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc))       MX_FENCE
+  MX_MFMA(3, 1)                       nxt.a[1] = frag(nA + 32 * BK, fo); MX_SNXT(nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc)) MX_FENCE
   MX_MFMA(3, 2)                                                                                                                      MX_FENCE
   MX_MFMA(3, 3)                                                                                                                      MX_FENCE
 #undef MX_MFMA
 #undef MX_FENCE
-#undef MX_SCALE
+#undef MX_LOAD
+#undef MX_SCUR
+#undef MX_SNXT
+  if constexpr (!kBf16 && !kOdd) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      nxt.sa[i] = cur.sa[i];
+      nxt.sb[i] = cur.sb[i];
+    }
+  }
   pin(acc, 2);
   // the next step's fragments are in registers before any wave can pass the
   // next barrier and start overwriting their stage
@@ -835,22 +865,25 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   read_b(st0, fa, wn, fo);
   read_a(st0, fa, wm, 0, 2, fo);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  // Steady state: stage s+1 is waited for with kVmem + kVmemFirst younger
-  // operations in flight (the loads of s+2 and the first part of s+3).  The
+  // Steady state: stage s+1 is waited for with the loads of s+2 and the first
+  // kVmemFirst loads of s+3 in flight (younger operations): an even step s
+  // has kVmem + kVmemFirst of them, an odd one kVmemOdd + kVmemFirst.  The
   // first two steps of a tile follow a tile store (or the drained prologue):
   // the tile's stores add tile_stores() younger operations, see finish_tile.
-  constexpr int kSteady = Elt<kBf16>::kVmem + kVmemFirst;
-  constexpr int kVmAfter = kSteady + tile_stores<kF32>() < 63 ? kSteady + tile_stores<kF32>() : 63;
+  constexpr int kSteadyE = Elt<kBf16>::kVmem + kVmemFirst;
+  constexpr int kSteadyO = (kBf16 ? Elt<kBf16>::kVmem : kVmemOdd) + kVmemFirst;
+  constexpr int kVmAfterE = kSteadyE + tile_stores<kF32>() < 63 ? kSteadyE + tile_stores<kF32>() : 63;
+  constexpr int kVmAfterO = kSteadyO + tile_stores<kF32>() < 63 ? kSteadyO + tile_stores<kF32>() : 63;
   do {
-    k_step<0, kVmAfter, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<1, kVmAfter, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<2, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<3, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<0, kVmAfterE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, kVmAfterO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<2, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<3, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
     while (c.s < c.t.steps) {
-      k_step<0, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<1, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<2, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<3, kSteady, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<0, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<2, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<3, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
     }
   } while (finish_tile<kF32, kWgrad, kBf16>(c, w, acc, wm, wn, st3));
   // loads past the last tile may still be writing LDS
