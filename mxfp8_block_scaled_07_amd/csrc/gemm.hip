@@ -98,6 +98,7 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 struct Sched {
   int32_t bound[kMaxGroups + 1];
   int32_t tiles_before[kMaxGroups + 1];
+  int64_t split[2];   // wgrad: the bounds of the workgroup's XCD range of tiles
 };
 
 // Inclusive wave scan (sum or max) over the 64 lanes.
@@ -155,6 +156,67 @@ __device__ __forceinline__ int find_group(const Sched& sc, int E, int64_t L) {
     if (uni(sc.tiles_before[mid]) <= L) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// wgrad work per tile of group e, in k steps: the ring steps of the group's
+// contraction range plus an allowance of 4 for the epilogue (an empty
+// group's tiles only store zeros).
+template <bool kBf16>
+__device__ __forceinline__ int64_t wgrad_unit(const Sched& sc, int e) {
+  const int32_t lo = sc.bound[e], hi = sc.bound[e + 1];
+  constexpr int32_t eb = kBf16 ? 2 : 1;
+  const int32_t kb = kBf16 ? lo * eb : lo & ~127;
+  const int32_t steps = hi > lo ? (hi * eb - kb + 63) / 64 : 0;
+  return ((steps + 3) & ~3) + 4;
+}
+
+// Wave 0 splits the wgrad tiles (T per group, group-major) into 8 ranges of
+// about equal work, one per XCD, and stores the bounds of XCD x's range:
+// the first tile L at which the work of the tiles before L reaches x/8 (and
+// (x+1)/8) of the total.
+template <bool kBf16>
+__device__ void wgrad_split(Sched& sc, int E, int64_t T, int x) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int64_t total = 0;
+    for (int base = 0; base < E; base += 64) {
+      int64_t u = base + lane < E ? wgrad_unit<kBf16>(sc, base + lane) : 0;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_xor(u, d, 64);
+        u += o;
+      }
+      total += u;
+    }
+    const int64_t W = total * T;                 // all lanes hold the same total
+    const int64_t goal0 = (int64_t)x * W, goal1 = (int64_t)(x + 1) * W;   // compared with 8 x work
+    int64_t carry = 0;
+    if (lane == 0) {
+      sc.split[0] = x == 0 ? 0 : (int64_t)E * T;
+      sc.split[1] = (int64_t)E * T;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int base = 0; base < E; base += 64) {
+      const int e = base + lane;
+      const int64_t u = e < E ? wgrad_unit<kBf16>(sc, e) : 0;
+      int64_t S = u;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t o = __shfl_up(S, d, 64);
+        if (lane >= d) S += o;
+      }
+      S += carry;
+      const int64_t P = S - u;
+      if (e < E) {
+        if (x > 0 && 8 * T * P <= goal0 && goal0 < 8 * T * S)
+          sc.split[0] = (int64_t)e * T + (goal0 - 8 * T * P + 8 * u - 1) / (8 * u);
+        if (x + 1 < 8 && 8 * T * P <= goal1 && goal1 < 8 * T * S)
+          sc.split[1] = (int64_t)e * T + (goal1 - 8 * T * P + 8 * u - 1) / (8 * u);
+      }
+      carry = __shfl(S, 63, 64);
+    }
+  }
+  __syncthreads();
 }
 
 struct Problem {
@@ -797,7 +859,10 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
 
 // Persistent workgroup: one per CU.  Logical tiles are split into 8 contiguous
 // ranges, one per XCD (workgroup b runs on XCD b % 8); the workgroups of an
-// XCD walk their range round robin.
+// XCD walk their range round robin.  Forward and dgrad tiles all have K / 64
+// steps: the ranges hold equal tile counts.  A wgrad tile's steps follow its
+// group's size (an empty group's tiles only store zeros): the ranges hold
+// equal work (wgrad_split).
 template <bool kF32, bool kWgrad, bool kBf16>
 __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __restrict__ offsets, int32_t E) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
@@ -809,10 +874,19 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   const int64_t n_tiles = kWgrad ? (p.K + BN - 1) / BN : (p.N + BN - 1) / BN;
   build_schedule(sc, offsets, E, p.m_cap, kWgrad ? 0 : (int32_t)n_tiles, kWgrad);
   const int64_t total = kWgrad ? (int64_t)E * m_tiles * n_tiles : (int64_t)uni(sc.tiles_before[E]);
-  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
   const int64_t x = blockIdx.x % kXcds;
-  const int64_t L_end = (x + 1) * per_xcd < total ? (x + 1) * per_xcd : total;
-  const int64_t L0 = x * per_xcd + blockIdx.x / kXcds;
+  int64_t L_begin, L_end;
+  if (kWgrad) {
+    // tiles differ in work (the groups' contraction lengths): ranges of equal work
+    wgrad_split<kBf16>(sc, E, m_tiles * n_tiles, (int)x);
+    L_begin = sc.split[0];
+    L_end = sc.split[1];
+  } else {
+    const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+    L_begin = x * per_xcd;
+    L_end = (x + 1) * per_xcd < total ? (x + 1) * per_xcd : total;
+  }
+  const int64_t L0 = L_begin + blockIdx.x / kXcds;
   if (L0 >= L_end) return;
   const Walk<kWgrad, kBf16> w{p, sc, E, m_tiles, n_tiles, (int64_t)(gridDim.x / kXcds), L_end};
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
