@@ -158,6 +158,22 @@ def test_edge_shapes_wgrad(lens, N, K):
         check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, dt)
 
 
+@pytest.mark.parametrize("lens,N,K", [
+    ([6016, 0, 32, 0, 0, 2048, 64, 0, 960], 512, 512),   # XCD range bounds inside the large group's tiles
+    ([0, 0, 0, 0], 256, 256),                            # all empty: every tile stores zeros
+    ([4096, 32], 96, 64),                                # fewer tiles than workgroups
+])
+def test_wgrad_work_split_extremes(lens, N, K):
+    """The wgrad tiles are split among XCDs by work (k steps per tile);
+    skewed and empty groups still give every dW element exactly once."""
+    g = np.random.default_rng(len(lens) + N + K)
+    off = np.concatenate([[0], np.cumsum(lens)])
+    cap = int(off[-1]) + 32
+    dyt_q, dyt_s = mx_rows(g, (N, cap), 1.0, 0.01)
+    xt_q, xt_s = mx_rows(g, (K, cap))
+    check_wgrad(dyt_q, dyt_s, xt_q, xt_s, off, mxa.MX_OUT_F32)
+
+
 def test_max_groups_fwd_and_wgrad():
     """2048 groups, the most one call takes, most of them tiny or empty:
     forward over ragged groups of 0 to 64 rows, wgrad over groups of 0, 32
