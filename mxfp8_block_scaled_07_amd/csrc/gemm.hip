@@ -25,24 +25,24 @@
 //
 // Tiling: 256 x 256 output tile per 256-thread workgroup (one per CU), 2 x 2
 // waves of 128 x 128 (4 x 4 MFMA tiles of 32 x 32 each), k steps of 64.
-// Operand tiles reach LDS through buffer loads that write LDS directly; a
-// load past a row or contraction bound returns zeros, which pads ragged
-// tiles for free.  A ring of 4 LDS stages keeps three k steps in flight: the
-// loads of step s+3 are issued during step s, so L2-miss latency has more
-// than two steps to hide.  Each step runs its first 8 MFMAs, waits for stage
-// s+1 (one barrier per step), and reads the fragments of step s+1 from LDS
-// during its last 8 MFMAs, so a step never starts on an LDS read.
-// A 128-byte line of an operand row holds two k steps.  The loads of an odd
-// step (second halves of lines) run in the reverse order of the even step's,
-// so the lines fetched last for one step are the first the next one asks
-// for and are still in the CU's L1; and since both steps of a 128-wide scale
-// panel use the same panel dword, odd steps load no scales and take the
-// even step's dwords from registers.
-// LDS rows are 64 B with the 16-byte chunks XOR-swizzled by row (conflict
-// free for the fragment reads).  Workgroups are persistent (one per CU) and
-// walk the output tiles of their XCD's share in an order where concurrently
-// running tiles share operand rows in that XCD's L2; the loads run ahead
-// across tile boundaries.
+// Operands are loaded in k lines of 128 bytes per row (two k steps): each
+// buffer load writes 8 rows x 128 bytes straight into LDS, so every request
+// is a whole 128-byte line (a 16-row x 64-byte load moves the same bytes in
+// twice as many half-line requests, and the load stream is what bounds this
+// kernel).  A load past a row or contraction bound returns zeros, which pads
+// ragged tiles for free.  Two LDS slots of one k line each: while the steps
+// of k line j run on one slot, k line j + 1 is loaded into the other.  The
+// even step of a k line reads the odd step's fragments too, so the odd step
+// frees its slot with a barrier at its start and loads the k line after next
+// into it, one load per MFMA slot; at its middle it waits for k line j + 1
+// (one wait and two barriers per k line).  The next step's fragments are
+// always read during the second half of a step, so a step never starts on
+// an LDS read.  Both steps of a k line use the same 128-wide scale panel
+// dword, read once.  LDS rows (128 B) are XOR-swizzled by 16-byte chunk
+// (conflict free for the fragment reads).  Workgroups are persistent (one
+// per CU) and walk the output tiles of their XCD's share in an order where
+// concurrently running tiles share operand rows in that XCD's L2; the loads
+// run ahead across tile boundaries.
 
 #include "mx_device.h"
 
@@ -58,28 +58,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BM = 256, BN = 256, BK = 64;
 constexpr int kThreads = 256;
-constexpr int kCodeBytes = BM * BK;                     // one operand, one stage (16 KB)
-constexpr int kScaleOff = 2 * kCodeBytes;               // A scale dwords, then B scale dwords
-constexpr int kStageBytes = 2 * kCodeBytes + 2 * BM * 4;
 constexpr int kXcds = 8;
 constexpr int kMaxGroups = 2048;                        // experts per grouped GEMM call
 constexpr uint32_t kOob = 0x80000000u;                  // voffset that reads as zero
-// Vector-memory instructions per wave per stage: 4 + 4 code blocks of 1 KB
-// and, for even k steps, one scale dword per lane for A and for B (odd steps:
-// kVmemOdd).  kVmemFirst of them are issued before the mid-step wait, the
-// rest after it.
-constexpr int kVmem = 10;
-constexpr int kVmemOdd = 8;
-constexpr int kVmemFirst = 5;
+// k lines: 128 bytes of each operand row (two k steps), loaded as whole
+// lines.  An LDS slot holds one k line of the tile: A rows 0-127, B rows
+// 0-127, A rows 128-255, B rows 128-255 (16 KB each, 128-byte rows), then
+// the A and B scale dwords.
+constexpr int kLine = 2 * BK;
+constexpr int kRegion = 128 * kLine;
+constexpr int kSlotScale = 4 * kRegion;
+constexpr int kSlotBytes = 4 * kRegion + 2 * BM * 4;
+constexpr int kEpiOff = 2 * kRegion;   // the epilogue stages through rows 128-255 and the scales
 
-// The bf16 baseline runs the same kernel with bf16 operands: a 64-byte LDS
-// row holds 32 bf16, so a k step contracts 32 elements with two
+// The bf16 baseline runs the same kernel with bf16 operands: 64 bytes of a
+// row hold 32 bf16, so a k step contracts 32 elements with two
 // V_MFMA_F32_32X32X16_BF16 per 32 x 32 tile (the same MFMA cycles and LDS
 // bytes per step as one scaled FP8 MFMA of 64), and there are no scales.
 template <bool kBf16>
 struct Elt {
   static constexpr int kBytes = kBf16 ? 2 : 1;          // bytes per operand element
-  static constexpr int kVmem = kBf16 ? 8 : mx::kVmem;   // vector-memory instructions per wave per stage
 };
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in
@@ -87,11 +85,9 @@ struct Elt {
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
 
-// 16-byte chunk swizzle of LDS row r (rows are 64 B = 4 chunks).  The
-// fragment reads (ds_read_b128) of 8 or 16 consecutive lanes cover 8 or 16
-// consecutive rows at one chunk column; this XOR sends them to distinct bank
-// groups in both cases.  Depends on r mod 16 only.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// 16-byte chunk swizzle of a 128-byte LDS row: 16 consecutive rows read at
+// one chunk column fall in 16 distinct bank groups.
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // Group schedule shared by the workgroup: clamped, monotone group bounds and
 // (row-grouped problems) the running count of tiles before each group.
@@ -165,7 +161,7 @@ template <bool kBf16>
 __device__ __forceinline__ int64_t wgrad_unit(const Sched& sc, int e) {
   const int32_t lo = sc.bound[e], hi = sc.bound[e + 1];
   constexpr int32_t eb = kBf16 ? 2 : 1;
-  const int32_t kb = kBf16 ? lo * eb : lo & ~127;
+  const int32_t kb = (lo * eb) & ~127;
   const int32_t steps = hi > lo ? (hi * eb - kb + 63) / 64 : 0;
   return ((steps + 3) & ~3) + 4;
 }
@@ -325,7 +321,7 @@ __device__ __forceinline__ Coord coord(const Problem& p, const Sched& sc, int E,
     // k in bytes of an operand row; MX steps start at the group's 128-row
     // scale panel, bf16 steps at the group's first row
     constexpr int32_t eb = Elt<kBf16>::kBytes;
-    c.k_begin = kBf16 ? lo * eb : lo & ~127;
+    c.k_begin = (lo * eb) & ~127;
     c.k_lo = lo * eb;
     c.k_hi = hi * eb;
     c.steps = hi > lo ? (c.k_hi - c.k_begin + BK - 1) / BK : 0;
@@ -393,19 +389,26 @@ struct Walk {
 // of LDS block 4w + i (16 rows x 64 B): block row 16(4w + i) + l/4, LDS slot
 // l & 3, holding the global chunk (l & 3) ^ swz(row).  Scale loads: lane l
 // of wave w fetches the dword of tile row 64w + l.
+
+// Per-lane constants of the loads.  Code load i (0..7) of wave w covers 8
+// rows x 128 bytes: tile rows 128 (i >> 2) + 8 (4 (i & 3) + w) + l / 8, LDS
+// chunk l & 7 holding the global chunk (l & 7) ^ swz8(row).  The chunk is
+// the same for all 8 loads of a lane.  Scale loads: lane l of wave w fetches
+// the dword of tile row 64 w + l.
 struct LaneLoads {
-  uint32_t voff[4];   // row * ld + 16 * chunk
-  int32_t kc[4];      // 16 * chunk
+  uint32_t voff[8];   // row * ld + 16 * chunk
+  int32_t kc;         // 16 * chunk
   int32_t srow;       // 64 w + l
 };
 
-// k steps a tile occupies in the 4-stage ring: its own rounded up to a
-// multiple of 4, so every tile starts on stage 0 and the ring can be unrolled
-// with a single loop exit; the padding steps load zeros and add zeros.
+// k steps a tile occupies in the ring: its own rounded up to a multiple of 4
+// (two k lines per LDS slot pair), so every tile starts on slot 0 and the
+// ring can be unrolled with a single loop exit; the padding steps load
+// zeros and add zeros.
 __device__ __forceinline__ int32_t ring_steps(int32_t steps) { return (steps + 3) & ~3; }
 
-// The loader walks the same tiles as the compute side, three k steps ahead,
-// skipping tiles without k steps.
+// The loader walks the same tiles as the compute side, two k lines ahead,
+// skipping tiles without k steps.  s counts k steps (2 per k line).
 struct Loader {
   LoadTile t;
   int64_t L;
@@ -429,7 +432,7 @@ __device__ __forceinline__ void loader_seek(Loader& ld, const Walk<kWgrad, kBf16
 // One LDS-direct buffer load (16 B or 4 B per lane) into LDS at byte lds
 // (+ 16 or 4 x lane).  Written as inline asm so the compiler neither tracks
 // it nor adds waits for it: every wait on these loads is explicit (vmcnt in
-// stage_barrier), and the stage a load writes is never read before that
+// stage_barrier), and the slot a load writes is never read before that
 // wait and a barrier.  M0 holds the LDS address; nothing else in these
 // kernels uses M0 (gfx9 LDS instructions do not read it).
 __device__ __forceinline__ void dma16(const v4u& r, uint32_t lds, uint32_t voff, uint32_t soff) {
@@ -450,75 +453,60 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
-// The loads of the loader's current k step into one LDS stage: 10
-// instructions per wave for an even step (A0 B0 A1 B1 A2 B2 A3 B3 sA sB),
-// the 8 code loads in reverse order for an odd one, issued one by one
-// between the MFMAs.  A loader past its last tile issues the same
-// instructions with out-of-range offsets (they read zeros), so every even
-// (odd) step issues exactly kVmem (kVmemOdd) instructions per wave.  Every
-// tile starts on ring stage 0 (the ring holds a multiple of 4 steps), so a
-// step's parity is that of its ring stage; for MX operands k_begin is a
-// multiple of 128 bytes, so steps 2j and 2j + 1 cover one scale panel.
+// The loads of one k line into one LDS slot: 18 instructions per wave.
+// Loads 0..7 (rows 0-127 of A and B: A0 B0 A1 B1 A2 B2 A3 B3) are issued in
+// the second half of an odd step, loads 8..15 (rows 128-255) and 16, 17 (the
+// A and B scale dwords) in the next even step.  A loader past its last tile
+// issues the same instructions with out-of-range offsets (they read zeros).
 struct LoadPlan {
   v4u aq, bq, as, bs;
-  uint32_t v[4];       // code voffsets (out of range where the chunk is outside [k_lo, k_hi))
-  uint32_t soff;       // k0
+  uint32_t v[8];       // code voffsets (out of range where the lane's chunk is outside [k_lo, k_hi))
+  uint32_t soff;       // k line start
   uint32_t sa, sb;     // scale voffsets
   uint32_t pa, pb;     // scale panel offsets
-  uint32_t dst;        // LDS address of the stage + this wave's first code block
-  uint32_t sdst;       // LDS address of the stage's scales + this wave's rows
+  uint32_t dst;        // LDS address of the slot + this wave's first 1 KB block
+  uint32_t sdst;       // LDS address of the slot's scales + this wave's rows
 };
 
-__device__ __forceinline__ LoadPlan plan_loads(const Loader& ld, const LaneLoads& ll, const uint8_t* stage,
-                                               int64_t pstride_a, int64_t pstride_b) {
+__device__ __forceinline__ LoadPlan plan_line(const Loader& ld, const LaneLoads& ll, const uint8_t* slot,
+                                              int64_t pstride_a, int64_t pstride_b) {
   LoadPlan pl;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int32_t k0 = ld.t.k_begin + BK * ld.s;
-  // chunks outside [k_lo, k_hi) occur in a tile's first or last steps and in
-  // its padding steps (which read nothing but zeros)
+  const int32_t kl = ld.t.k_begin + BK * ld.s;   // a multiple of 128 bytes
+  const int32_t k = kl + ll.kc;
+  const bool ok = ld.valid & (k >= ld.t.k_lo) & (k < ld.t.k_hi);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int32_t k = k0 + ll.kc[i];
-    const bool ok = ld.valid & (k >= ld.t.k_lo) & (k < ld.t.k_hi);
-    pl.v[i] = ok ? ll.voff[i] : kOob;
-  }
+  for (int i = 0; i < 8; ++i) pl.v[i] = ok ? ll.voff[i] : kOob;
   pl.aq = ld.t.aq;
   pl.bq = ld.t.bq;
   pl.as = ld.t.as;
   pl.bs = ld.t.bs;
-  pl.soff = ld.valid ? (uint32_t)k0 : 0u;
-  // a step with no valid k (ring padding) reads no scales: its panel offset
-  // may lie past the scale tensor
-  // (scales are loaded by even steps, for both steps of their 128-wide panel)
-  const bool kin = ld.valid & (k0 < ld.t.k_hi) & (k0 + 2 * BK > ld.t.k_lo);
+  pl.soff = ld.valid ? (uint32_t)kl : 0u;
+  // a k line with no valid k (ring padding) reads no scales: its panel
+  // offset may lie past the scale tensor
+  const bool kin = ld.valid & (kl < ld.t.k_hi) & (kl + kLine > ld.t.k_lo);
   pl.sa = (kin & (ll.srow < ld.t.rows_a)) ? 4u * (uint32_t)ll.srow : kOob;
   pl.sb = (kin & (ll.srow < ld.t.rows_b)) ? 4u * (uint32_t)ll.srow : kOob;
-  pl.pa = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_a : 0u;
-  pl.pb = ld.valid ? (uint32_t)(k0 >> 7) * (uint32_t)pstride_b : 0u;
-  pl.dst = lds_addr(stage) + (uint32_t)(4 * w * 1024);
-  pl.sdst = lds_addr(stage) + (uint32_t)(kScaleOff + w * 256);
+  pl.pa = ld.valid ? (uint32_t)(kl >> 7) * (uint32_t)pstride_a : 0u;
+  pl.pb = ld.valid ? (uint32_t)(kl >> 7) * (uint32_t)pstride_b : 0u;
+  pl.dst = lds_addr(slot) + (uint32_t)(w * 1024);
+  pl.sdst = lds_addr(slot) + (uint32_t)(kSlotScale + w * 256);
   return pl;
 }
 
-// Load number n (0..9) of a plan; the bf16 operands have no scale loads (8, 9).
+// Load number n (0..17) of a plan; the bf16 operands have no scale loads.
 template <bool kBf16>
 __device__ __forceinline__ void load_n(const LoadPlan& pl, int n) {
-  if (n < 8) {
-    const int i = n >> 1;
-    if (n & 1) dma16(pl.bq, pl.dst + kCodeBytes + i * 1024, pl.v[i], pl.soff);
-    else dma16(pl.aq, pl.dst + i * 1024, pl.v[i], pl.soff);
+  if (n < 16) {
+    const int i = (n < 8 ? 0 : 4) + ((n & 7) >> 1);   // code load i: rows 128 (i >> 2) + ...
+    const uint32_t off = (uint32_t)((2 * (i >> 2) + (n & 1)) * kRegion + 4 * (i & 3) * 1024);
+    dma16((n & 1) ? pl.bq : pl.aq, pl.dst + off, pl.v[i], pl.soff);
   } else if (kBf16) {
-  } else if (n == 8) {
+  } else if (n == 16) {
     dma4(pl.as, pl.sdst, pl.sa, pl.pa);
   } else {
     dma4(pl.bs, pl.sdst + BM * 4, pl.sb, pl.pb);
   }
-}
-
-template <bool kBf16>
-__device__ __forceinline__ void issue_all(const LoadPlan& pl) {
-#pragma unroll
-  for (int n = 0; n < kVmem; ++n) load_n<kBf16>(pl, n);
 }
 
 // The MFMA operands of one k step for one wave.  Scales hold the raw panel
@@ -528,51 +516,42 @@ struct Frags {
   int sa[4], sb[4];
 };
 
-// Lane offsets of a fragment inside a 32-row block: row r = l & 31, chunks
-// h and h + 2 (h = l >> 5), swizzled.  swz depends on the row's bits 1..3
-// only, so rows 32 i + r of any block share these offsets and a fragment is
-// read at (block base) + offset with the block base an immediate.
+// Lane offsets of a fragment inside a 32-row block of 128-byte rows, for the
+// first (p = 0) and second (p = 1) k step of the line: row r = l & 31,
+// chunks 4 p + h and 4 p + 2 + h (h = l >> 5), swizzled.  swz8 depends on
+// the row's bits 1..3 only, so rows 32 i + r of any block share these
+// offsets and a fragment is read at (block base) + offset with the block
+// base an immediate.
 struct FragOff {
-  int lo, hi, sc;   // code chunk offsets, scale dword offset
+  int lo[2], hi[2], sc;   // code chunk offsets per step parity, scale dword offset
 };
 
 __device__ __forceinline__ FragOff frag_off() {
   const int lane = threadIdx.x & 63;
   const int r = lane & 31, h = lane >> 5;
-  const int c = h ^ swz(r);
-  return FragOff{r * BK + 16 * c, r * BK + 16 * (c ^ 2), 4 * r};
+  FragOff f;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    f.lo[p] = r * kLine + 16 * ((4 * p + h) ^ swz8(r));
+    f.hi[p] = r * kLine + 16 * ((4 * p + 2 + h) ^ swz8(r));
+  }
+  f.sc = 4 * r;
+  return f;
 }
 
+template <int P>
 __device__ __forceinline__ v8i frag(const uint8_t* blk, const FragOff& fo) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(blk + fo.lo);
-  const uint4 hi = *reinterpret_cast<const uint4*>(blk + fo.hi);
+  const uint4 lo = *reinterpret_cast<const uint4*>(blk + fo.lo[P]);
+  const uint4 hi = *reinterpret_cast<const uint4*>(blk + fo.hi[P]);
   v8i v;
   v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
   v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
   return v;
 }
 
-// Fragments of A blocks i0 .. i1-1 of a stage (with their scale dwords).
-__device__ __forceinline__ void read_a(const uint8_t* st, Frags& f, int wm, int i0, int i1, const FragOff& fo) {
-  const uint8_t* A = st + wm * 128 * BK;
-  const uint8_t* S = st + kScaleOff + wm * 128 * 4;
-#pragma unroll
-  for (int i = i0; i < i1; ++i) {
-    f.a[i] = frag(A + 32 * i * BK, fo);
-    f.sa[i] = *reinterpret_cast<const int*>(S + 32 * i * 4 + fo.sc);
-  }
-}
-
-// All 4 B fragments of a stage (with their scale dwords).
-__device__ __forceinline__ void read_b(const uint8_t* st, Frags& f, int wn, const FragOff& fo) {
-  const uint8_t* B = st + kCodeBytes + wn * 128 * BK;
-  const uint8_t* S = st + kScaleOff + BM * 4 + wn * 128 * 4;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f.b[j] = frag(B + 32 * j * BK, fo);
-    f.sb[j] = *reinterpret_cast<const int*>(S + 32 * j * 4 + fo.sc);
-  }
-}
+// Base of a wave's 128 rows of A (wm) or B (wn) in a slot.
+__device__ __forceinline__ const uint8_t* a_base(const uint8_t* slot, int wm) { return slot + 2 * wm * kRegion; }
+__device__ __forceinline__ const uint8_t* b_base(const uint8_t* slot, int wn) { return slot + (2 * wn + 1) * kRegion; }
 
 // The E8M0 byte a lane passes to the MFMA (bits 7:0 of the operand): byte
 // sel / 8 of the panel dword, or 0 (2^-127, applied to zero codes) when the
@@ -602,16 +581,6 @@ __device__ __forceinline__ v16f mma(const v8i& b, const v8i& a, const v16f& c, i
   }
 }
 
-// MFMAs of A fragments i0, i0 + 1 against the 4 B fragments.
-__device__ __forceinline__ void mma_half(const Frags& f, v16f (&acc)[4][4], int i0) {
-#pragma unroll
-  for (int i = i0; i < i0 + 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], acc[i][j], 0, 0, 0, f.sb[j], 0,
-                                                                  f.sa[i]);
-}
-
 // The MFMA results are only consumed tiles later, so the compiler would sink
 // MFMAs below the step's waits and barrier; an empty asm that claims to update
 // the accumulators keeps each half in place.
@@ -631,23 +600,20 @@ __device__ __forceinline__ void zero_acc(v16f (&acc)[4][4]) {
 }
 
 // Tile epilogue, staged through LDS so that every global store writes whole
-// 128-byte lines.  Each wave owns a quarter of an LDS stage, 32 rows x 272 B
+// 128-byte lines.  Each wave owns a quarter of the staging area (rows
+// 128-255 and the scales of LDS slot 1), 32 rows x 272 B
 // (64 fp32 columns + 16 B of padding, which puts the 32 rows written by one
 // ds_write_b128 in distinct bank groups).  For each 32 x 64 part of its
 // 128 x 128 result, a wave writes the fp32 accumulators (straight from the
 // accumulator registers), reads them back 8 consecutive columns per lane,
 // converts, and stores 8 rows x 64 columns per instruction.  Rows and
-// columns outside the tile get out-of-range offsets and are dropped, so
-// every wave issues exactly kTileStores store instructions per tile.
+// columns outside the tile get out-of-range offsets and are dropped.
 constexpr int kEpiPitch = 272;
 // cache policy of the output stores: non-temporal (streamed; the output is
 // not read again by this kernel)
 constexpr int kStoreNt = 2;
 constexpr int kEpiSlice = 32 * kEpiPitch;
-static_assert(4 * kEpiSlice == kStageBytes, "the epilogue uses one LDS stage");
-
-template <bool kF32>
-constexpr int tile_stores() { return kF32 ? 64 : 32; }
+static_assert(4 * kEpiSlice == kSlotBytes - kEpiOff, "the epilogue uses rows 128-255 and the scales of a slot");
 
 template <bool kF32>
 __device__ __forceinline__ void store_tile(const OutTile& o, const v16f (&acc)[4][4], int wm, int wn,
@@ -714,16 +680,16 @@ struct Cursor {
 // steps, storing exact zeros for tiles without any (wgrad of an empty group).
 // Returns false when the workgroup has no tiles left.
 //
-// Vector memory operations complete in issue order, stores included, and
-// every tile store issues exactly tile_stores() instructions per wave.  So
-// the two mid-step waits right after a tile store have at least that many
-// more younger operations behind the loads they wait for (see kVmAfterE/O).
-// The epilogue stages through LDS stage 3, which the next step's loads
-// overwrite: a barrier after it keeps every wave's reads ahead of them.
+// Vector memory operations complete in issue order, stores included: the
+// next odd step's wait covers the tile's stores too.  The epilogue stages
+// through rows 128-255 and the scales of slot 1 (the loads in flight at a
+// tile end write its rows 0-127); the next even step's loads overwrite the
+// staging area, and a barrier after the epilogue keeps every wave's reads
+// ahead of them.
 template <bool kF32, bool kWgrad, bool kBf16>
 __device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad, kBf16>& w, v16f (&acc)[4][4], int wm, int wn,
-                                            uint8_t* st3) {
-  store_tile<kF32>(c.t, acc, wm, wn, st3);
+                                            uint8_t* stage) {
+  store_tile<kF32>(c.t, acc, wm, wn, stage);
   zero_acc(acc);
   c.s = 0;
   bool more = true;
@@ -735,7 +701,7 @@ __device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad, kBf16>
     }
     c.t = out_tile<kWgrad>(w.p, w.at(c.L));
     if (c.t.steps > 0) break;
-    store_tile<kF32>(c.t, acc, wm, wn, st3);
+    store_tile<kF32>(c.t, acc, wm, wn, stage);
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   asm volatile("" ::: "memory");
@@ -744,10 +710,10 @@ __device__ __forceinline__ bool finish_tile(Cursor& c, const Walk<kWgrad, kBf16>
   return more;
 }
 
-// Wait until the own loads of stage s+1 are complete (kVm younger vector
-// memory operations may stay in flight), then a workgroup barrier.  The
-// barrier is a bare s_barrier: the fence of __syncthreads would also wait
-// for the loads of the later stages.  Compiler-level memory clobbers keep
+// Wait until the own loads of the next k line are complete (kVm younger
+// vector memory operations may stay in flight), then a workgroup barrier.
+// The barrier is a bare s_barrier: the fence of __syncthreads would also wait
+// for the loads of the k line after it.  Compiler-level memory clobbers keep
 // LDS accesses from moving across it.
 template <int kVm>
 __device__ __forceinline__ void stage_barrier() {
@@ -757,90 +723,101 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// One k step on stage CUR.  On entry `cur` holds the step's B fragments and
-// A fragments 0, 1 (read during the previous step); A fragments 2, 3 are read
-// during the first half.  The loads of the step three ahead go to stage
-// (CUR + 3) % 4, which every wave finished reading before the previous
-// step's barrier; after this step's barrier the B and first two A fragments
-// of the next step are read from stage (CUR + 1) % 4 into `nxt`.
-//
-// The step is written as 16 slots, one MFMA each, with the loads and LDS
-// reads spread over them; scheduling fences between slots keep that order.
-template <int CUR, int kVm, bool kWgrad, bool kBf16>
-__device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3, Frags& cur, Frags& nxt,
-                                       v16f (&acc)[4][4], Loader& ld, const LaneLoads& ll, Cursor& c,
+// One k step: the first (ODD = false) or second half of the k line in slot
+// SLOT.  Even step: on entry `cur` holds the step's B fragments and A
+// fragments 0, 1; A fragments 2, 3 are read during the first half, and all
+// eight fragments of the odd step (same slot, other k half) during the
+// second half.  Odd step: everything is in registers; a barrier at the start
+// frees the slot (every wave has read it), the loads of the k line after
+// next go into it from slot 0, the mid-step wait (vmcnt(8): those loads may
+// still be in flight) and barrier make the next k line visible, and the
+// second half reads the next even step's fragments from the other slot.
+// LOADS: which loads of the current plan the step issues, one per slot from
+// its first slot: even steps 8..17 (E8) or 16..17 (E16); odd steps 0..7
+// (O8) or 0..15 (O16).
+constexpr int kE8 = 0, kE16 = 1, kO8 = 2, kO16 = 3;
+template <int SLOT, bool ODD, int LOADS, bool kWgrad, bool kBf16>
+__device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, Frags& cur, Frags& nxt, v16f (&acc)[4][4],
+                                       Loader& ld, LoadPlan& plan, const LaneLoads& ll, Cursor& c,
                                        const Walk<kWgrad, kBf16>& w, int wm, int wn, int64_t pa, int64_t pb,
                                        const FragOff& fo) {
-  uint8_t* const nst = CUR == 0 ? s1 : CUR == 1 ? s2 : CUR == 2 ? s3 : s0;   // stage of step s+1
-  uint8_t* const lst = CUR == 0 ? s3 : CUR == 1 ? s0 : CUR == 2 ? s1 : s2;   // stage of step s+3
-  uint8_t* const cst = CUR == 0 ? s0 : CUR == 1 ? s1 : CUR == 2 ? s2 : s3;   // stage of step s
+  uint8_t* const cst = SLOT == 0 ? s0 : s1;
+  uint8_t* const ost = SLOT == 0 ? s1 : s0;
+  constexpr int P = ODD ? 1 : 0;
   const int h = (threadIdx.x >> 5) & 1;
-  // the step's scale bytes: byte 2 * (k step parity) + h of the panel dword.
-  // Blocks outside the tile's contraction range load zero codes; their scale
-  // bytes are replaced by 0: a wgrad panel can hold blocks of the
-  // neighbouring groups, and a NaN scale (0xFF) of another group must not
-  // reach this group's sums.
-  const int sel = 8 * (2 * (c.s & 1) + h);
+  const int sel = 8 * (2 * P + h);
   const int32_t bi = 2 * c.s + h;
   const uint32_t bok = (bi >= c.t.blk_lo) & (bi < c.t.blk_hi) ? 8u : 0u;
-  const LoadPlan pl = plan_loads(ld, ll, lst, pa, pb);
-  const uint8_t* A = cst + wm * 128 * BK;
-  const uint8_t* SA = cst + kScaleOff + wm * 128 * 4;
-  const uint8_t* nA = nst + wm * 128 * BK;
-  const uint8_t* nSA = nst + kScaleOff + wm * 128 * 4;
-  const uint8_t* nB = nst + kCodeBytes + wn * 128 * BK;
-  const uint8_t* nSB = nst + kScaleOff + BM * 4 + wn * 128 * 4;
-  // Steps 2j and 2j + 1 share their panel dwords (raw in cur.sa / cur.sb):
-  // an even step reads them from LDS and hands them on to the odd step, whose
-  // stage holds no scales.  The loads issued here are for step s+3, of the
-  // other parity: an even step issues the odd step's 8 code loads, reversed.
-  constexpr bool kOdd = (CUR & 1) == 1;
+  const uint8_t* A = a_base(cst, wm);
+  const uint8_t* B = b_base(cst, wn);
+  const uint8_t* SA = cst + kSlotScale + wm * 128 * 4;
+  const uint8_t* nA = a_base(ost, wm);
+  const uint8_t* nB = b_base(ost, wn);
+  const uint8_t* nSA = ost + kSlotScale + wm * 128 * 4;
+  const uint8_t* nSB = ost + kSlotScale + BM * 4 + wn * 128 * 4;
+  if constexpr (ODD) {
+    plan = plan_line(ld, ll, cst, pa, pb);
+    ld.s += 2;
+    loader_seek<kWgrad, kBf16>(ld, w);
+    // every wave has read this slot (the reads completed at the end of the
+    // even step): the loads below may overwrite it
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
   int xa[4] = {0, 0, 0, 0}, xb[4] = {0, 0, 0, 0};   // the step's scale bytes
   if constexpr (!kBf16) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) xb[j] = scale_byte(cur.sb[j], sel, bok);
     xa[0] = scale_byte(cur.sa[0], sel, bok);
     xa[1] = scale_byte(cur.sa[1], sel, bok);
+    if constexpr (ODD) {
+      xa[2] = scale_byte(cur.sa[2], sel, bok);
+      xa[3] = scale_byte(cur.sa[3], sel, bok);
+    }
   }
   __builtin_amdgcn_sched_barrier(0);
+  constexpr int L0 = LOADS == kE8 ? 8 : LOADS == kE16 ? 16 : 0;
+  constexpr int LN = LOADS == kE8 ? 10 : LOADS == kE16 ? 2 : LOADS == kO8 ? 8 : 16;
 #define MX_MFMA(i, j) acc[i][j] = mma<kBf16>(cur.b[j], cur.a[i], acc[i][j], xb[j], xa[i]);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
-#define MX_LOAD(n) load_n<kBf16>(pl, !kOdd ? 7 - (n) : (n));
-#define MX_SCUR(x) if constexpr (!kBf16 && !kOdd) { x; }
-#define MX_SNXT(x) if constexpr (!kBf16 && kOdd) { x; }
-  // first half: MFMAs of A fragments 0, 1; loads 0..4; A fragments 2, 3
-  MX_MFMA(0, 0) MX_LOAD(0) cur.a[2] = frag(A + 64 * BK, fo);                             MX_FENCE
-  MX_MFMA(0, 1) MX_LOAD(1) MX_SCUR(cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc)) MX_FENCE
-  MX_MFMA(0, 2) MX_LOAD(2) cur.a[3] = frag(A + 96 * BK, fo);                             MX_FENCE
-  MX_MFMA(0, 3) MX_LOAD(3) MX_SCUR(cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc)) MX_FENCE
-  MX_MFMA(1, 0) MX_LOAD(4)                                                               MX_FENCE
-  MX_MFMA(1, 1)                                                                       MX_FENCE
-  MX_MFMA(1, 2)                                                                       MX_FENCE
-  MX_MFMA(1, 3)                                                                       MX_FENCE
+#define MX_L(t) if constexpr ((t) < LN) load_n<kBf16>(plan, L0 + (t));
+#define MX_E(x) if constexpr (!ODD) { x; }
+#define MX_SE(x) if constexpr (!kBf16 && !ODD) { x; }
+#define MX_SO(x) if constexpr (!kBf16 && ODD) { x; }
+  // first half: MFMAs of A fragments 0, 1; an even step reads A fragments 2, 3
+  MX_MFMA(0, 0) MX_L(0) MX_E(cur.a[2] = frag<0>(A + 64 * kLine, fo))                               MX_FENCE
+  MX_MFMA(0, 1) MX_L(1) MX_SE(cur.sa[2] = *reinterpret_cast<const int*>(SA + 256 + fo.sc))         MX_FENCE
+  MX_MFMA(0, 2) MX_L(2) MX_E(cur.a[3] = frag<0>(A + 96 * kLine, fo))                               MX_FENCE
+  MX_MFMA(0, 3) MX_L(3) MX_SE(cur.sa[3] = *reinterpret_cast<const int*>(SA + 384 + fo.sc))         MX_FENCE
+  MX_MFMA(1, 0) MX_L(4)                                                                            MX_FENCE
+  MX_MFMA(1, 1) MX_L(5)                                                                            MX_FENCE
+  MX_MFMA(1, 2) MX_L(6)                                                                            MX_FENCE
+  MX_MFMA(1, 3) MX_L(7)                                                                            MX_FENCE
   pin(acc, 0);
-  // stage s+1 complete: own loads, then everyone's
-  stage_barrier<kVm>();
+  if constexpr (ODD) stage_barrier<8>();   // the next k line complete (8 younger loads may remain)
   MX_FENCE
-  if constexpr (!kBf16) {
+  if constexpr (!kBf16 && !ODD) {
     xa[2] = scale_byte(cur.sa[2], sel, bok);
     xa[3] = scale_byte(cur.sa[3], sel, bok);
   }
-  // second half: MFMAs of A fragments 2, 3; loads 5..9; the next step's B
-  // fragments and A fragments 0, 1
-  MX_MFMA(2, 0) MX_LOAD(5) nxt.b[0] = frag(nB, fo);           MX_SNXT(nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc))       MX_FENCE
-  MX_MFMA(2, 1) MX_LOAD(6) nxt.b[1] = frag(nB + 32 * BK, fo); MX_SNXT(nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc)) MX_FENCE
-  MX_MFMA(2, 2) MX_LOAD(7) nxt.b[2] = frag(nB + 64 * BK, fo); MX_SNXT(nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc)) MX_FENCE
-  MX_MFMA(2, 3) if constexpr (kOdd) load_n<kBf16>(pl, 8); nxt.b[3] = frag(nB + 96 * BK, fo); MX_SNXT(nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc)) MX_FENCE
-  MX_MFMA(3, 0) if constexpr (kOdd) load_n<kBf16>(pl, 9); nxt.a[0] = frag(nA, fo);           MX_SNXT(nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc))       MX_FENCE
-  MX_MFMA(3, 1)                       nxt.a[1] = frag(nA + 32 * BK, fo); MX_SNXT(nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc)) MX_FENCE
-  MX_MFMA(3, 2)                                                                                                                      MX_FENCE
-  MX_MFMA(3, 3)                                                                                                                      MX_FENCE
+  // second half: MFMAs of A fragments 2, 3; the next step's fragments (even:
+  // all eight, same slot, k half 1; odd: B0-3, A0, A1 and scales, other slot, k half 0)
+  MX_MFMA(2, 0) MX_L(8)  if constexpr (ODD) { nxt.b[0] = frag<0>(nB, fo); } else { nxt.b[0] = frag<1>(B, fo); } MX_SO(nxt.sb[0] = *reinterpret_cast<const int*>(nSB + fo.sc))       MX_FENCE
+  MX_MFMA(2, 1) MX_L(9)  if constexpr (ODD) { nxt.b[1] = frag<0>(nB + 32 * kLine, fo); } else { nxt.b[1] = frag<1>(B + 32 * kLine, fo); } MX_SO(nxt.sb[1] = *reinterpret_cast<const int*>(nSB + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 2) MX_L(10) if constexpr (ODD) { nxt.b[2] = frag<0>(nB + 64 * kLine, fo); } else { nxt.b[2] = frag<1>(B + 64 * kLine, fo); } MX_SO(nxt.sb[2] = *reinterpret_cast<const int*>(nSB + 256 + fo.sc)) MX_FENCE
+  MX_MFMA(2, 3) MX_L(11) if constexpr (ODD) { nxt.b[3] = frag<0>(nB + 96 * kLine, fo); } else { nxt.b[3] = frag<1>(B + 96 * kLine, fo); } MX_SO(nxt.sb[3] = *reinterpret_cast<const int*>(nSB + 384 + fo.sc)) MX_FENCE
+  MX_MFMA(3, 0) MX_L(12) if constexpr (ODD) { nxt.a[0] = frag<0>(nA, fo); } else { nxt.a[0] = frag<1>(A, fo); } MX_SO(nxt.sa[0] = *reinterpret_cast<const int*>(nSA + fo.sc))       MX_FENCE
+  MX_MFMA(3, 1) MX_L(13) if constexpr (ODD) { nxt.a[1] = frag<0>(nA + 32 * kLine, fo); } else { nxt.a[1] = frag<1>(A + 32 * kLine, fo); } MX_SO(nxt.sa[1] = *reinterpret_cast<const int*>(nSA + 128 + fo.sc)) MX_FENCE
+  MX_MFMA(3, 2) MX_L(14) MX_E(nxt.a[2] = frag<1>(A + 64 * kLine, fo))                                                                       MX_FENCE
+  MX_MFMA(3, 3) MX_L(15) MX_E(nxt.a[3] = frag<1>(A + 96 * kLine, fo))                                                                       MX_FENCE
 #undef MX_MFMA
 #undef MX_FENCE
-#undef MX_LOAD
-#undef MX_SCUR
-#undef MX_SNXT
-  if constexpr (!kBf16 && !kOdd) {
+#undef MX_L
+#undef MX_E
+#undef MX_SE
+#undef MX_SO
+  if constexpr (!kBf16 && !ODD) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       nxt.sa[i] = cur.sa[i];
@@ -848,12 +825,10 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
     }
   }
   pin(acc, 2);
-  // the next step's fragments are in registers before any wave can pass the
-  // next barrier and start overwriting their stage
+  // the next step's fragments are in registers before this wave reaches the
+  // next barrier, after which other waves may overwrite their slot
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   __builtin_amdgcn_sched_barrier(0);
-  ++ld.s;
-  loader_seek<kWgrad, kBf16>(ld, w);
   ++c.s;
 }
 
@@ -865,10 +840,8 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, uint8_t* s2, ui
 // equal work (wgrad_split).
 template <bool kF32, bool kWgrad, bool kBf16>
 __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __restrict__ offsets, int32_t E) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t st3[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[kSlotBytes];
   __shared__ Sched sc;
   const int64_t m_tiles = (p.N + BM - 1) / BM;  // wgrad only
   const int64_t n_tiles = kWgrad ? (p.K + BN - 1) / BN : (p.N + BN - 1) / BN;
@@ -896,12 +869,15 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   const int64_t pa = kWgrad ? 4 * p.N : 4 * p.m_cap;
   const int64_t pb = kWgrad ? 4 * p.K : 4 * (int64_t)E * p.N;
   LaneLoads ll;
+  {
+    const int rr = 8 * wave + (lane >> 3);   // region row of load 0 (load i adds 32 (i & 3))
+    const int ch = (lane & 7) ^ swz8(rr);
+    ll.kc = 16 * ch;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (4 * wave + i) + (lane >> 2);
-    const int ch = (lane & 3) ^ swz(row);
-    ll.voff[i] = (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)ch;
-    ll.kc[i] = 16 * ch;
+    for (int i = 0; i < 8; ++i) {
+      const int row = 128 * (i >> 2) + 32 * (i & 3) + rr;
+      ll.voff[i] = (uint32_t)row * (uint32_t)ldb + 16u * (uint32_t)ch;
+    }
   }
   ll.srow = 64 * wave + lane;
   v16f acc[4][4];
@@ -912,54 +888,60 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   c.s = 0;
   c.t = out_tile<kWgrad>(p, w.at(L0));
   while (c.t.steps == 0) {
-    store_tile<kF32>(c.t, acc, wm, wn, st3);
+    store_tile<kF32>(c.t, acc, wm, wn, st1 + kEpiOff);
     c.L += w.stride;
     if (c.L >= L_end) return;
     c.t = out_tile<kWgrad>(p, w.at(c.L));
   }
-  // loader: starts at the same tile; the prologue fills stages 0..2
+  // loader: starts at the same tile; the prologue loads k line 0 into slot 0
+  // and issues loads 0..7 of k line 1 (slot 1), as the odd step before the
+  // first even step would
   Loader ld;
   ld.L = c.L;
   ld.t = load_tile<kWgrad, kBf16>(p, w.at(c.L), E);
   ld.s = 0;
   ld.valid = true;
-  issue_all<kBf16>(plan_loads(ld, ll, st0, pa, pb));
-  ++ld.s;
+  LoadPlan plan = plan_line(ld, ll, st0, pa, pb);
+#pragma unroll
+  for (int n = 0; n < 18; ++n) load_n<kBf16>(plan, n);
+  ld.s += 2;
   loader_seek<kWgrad, kBf16>(ld, w);
-  issue_all<kBf16>(plan_loads(ld, ll, st1, pa, pb));
-  ++ld.s;
-  loader_seek<kWgrad, kBf16>(ld, w);
-  issue_all<kBf16>(plan_loads(ld, ll, st2, pa, pb));
-  ++ld.s;
-  loader_seek<kWgrad, kBf16>(ld, w);
-  // drain the prologue: the first two steps wait with vmcnt(63)
   stage_barrier<0>();
   const FragOff fo = frag_off();
   Frags fa, fb;
-  read_b(st0, fa, wn, fo);
-  read_a(st0, fa, wm, 0, 2, fo);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    fa.b[j] = frag<0>(b_base(st0, wn) + 32 * j * kLine, fo);
+    fa.sb[j] = *reinterpret_cast<const int*>(st0 + kSlotScale + BM * 4 + (wn * 128 + 32 * j) * 4 + fo.sc);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    fa.a[i] = frag<0>(a_base(st0, wm) + 32 * i * kLine, fo);
+    fa.sa[i] = *reinterpret_cast<const int*>(st0 + kSlotScale + (wm * 128 + 32 * i) * 4 + fo.sc);
+  }
+  plan = plan_line(ld, ll, st1, pa, pb);
+#pragma unroll
+  for (int n = 0; n < 8; ++n) load_n<kBf16>(plan, n);
+  ld.s += 2;
+  loader_seek<kWgrad, kBf16>(ld, w);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  // Steady state: stage s+1 is waited for with the loads of s+2 and the first
-  // kVmemFirst loads of s+3 in flight (younger operations): an even step s
-  // has kVmem + kVmemFirst of them, an odd one kVmemOdd + kVmemFirst.  The
-  // first two steps of a tile follow a tile store (or the drained prologue):
-  // the tile's stores add tile_stores() younger operations, see finish_tile.
-  constexpr int kSteadyE = Elt<kBf16>::kVmem + kVmemFirst;
-  constexpr int kSteadyO = (kBf16 ? Elt<kBf16>::kVmem : kVmemOdd) + kVmemFirst;
-  constexpr int kVmAfterE = kSteadyE + tile_stores<kF32>() < 63 ? kSteadyE + tile_stores<kF32>() : 63;
-  constexpr int kVmAfterO = kSteadyO + tile_stores<kF32>() < 63 ? kSteadyO + tile_stores<kF32>() : 63;
+  // Loads per k line (18 per wave): the odd step of slot 0 issues 0..15 of
+  // its plan and the next even step 16, 17; the odd step of slot 1 issues
+  // 0..7 only (it may end a tile, whose epilogue stages through its slot's
+  // rows 128-255) and the next even step 8..17.  Tiles hold a multiple of 4
+  // steps, so a tile always ends on the odd step of slot 1.
   do {
-    k_step<0, kVmAfterE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<1, kVmAfterO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<2, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<3, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<0, false, kE8, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<0, true, kO16, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, false, kE16, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, true, kO8, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
     while (c.s < c.t.steps) {
-      k_step<0, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<1, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<2, kSteadyE, kWgrad, kBf16>(st0, st1, st2, st3, fa, fb, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<3, kSteadyO, kWgrad, kBf16>(st0, st1, st2, st3, fb, fa, acc, ld, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<0, false, kE8, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<0, true, kO16, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, false, kE16, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, true, kO8, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
     }
-  } while (finish_tile<kF32, kWgrad, kBf16>(c, w, acc, wm, wn, st3));
+  } while (finish_tile<kF32, kWgrad, kBf16>(c, w, acc, wm, wn, st1 + kEpiOff));
   // loads past the last tile may still be writing LDS
   __builtin_amdgcn_s_waitcnt(0);
 }
