@@ -732,10 +732,10 @@ __device__ __forceinline__ void stage_barrier() {
 // next go into it from slot 0, the mid-step wait (vmcnt(8): those loads may
 // still be in flight) and barrier make the next k line visible, and the
 // second half reads the next even step's fragments from the other slot.
-// LOADS: which loads of the current plan the step issues, one per slot from
-// its first slot: even steps 8..17 (E8) or 16..17 (E16); odd steps 0..7
-// (O8) or 0..15 (O16).
-constexpr int kE8 = 0, kE16 = 1, kO8 = 2, kO16 = 3;
+// LOADS: which loads of the current plan the step issues: even steps 8..17
+// (kE8) or 10..17 (kE10), two in every three MFMA slots from the first; odd
+// steps 0..7 (kO8) or 0..9 (kO10), one per slot from the first.
+constexpr int kE8 = 0, kE10 = 1, kO8 = 2, kO10 = 3;
 template <int SLOT, bool ODD, int LOADS, bool kWgrad, bool kBf16>
 __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, Frags& cur, Frags& nxt, v16f (&acc)[4][4],
                                        Loader& ld, LoadPlan& plan, const LaneLoads& ll, Cursor& c,
@@ -777,11 +777,17 @@ __device__ __forceinline__ void k_step(uint8_t* s0, uint8_t* s1, Frags& cur, Fra
     }
   }
   __builtin_amdgcn_sched_barrier(0);
-  constexpr int L0 = LOADS == kE8 ? 8 : LOADS == kE16 ? 16 : 0;
-  constexpr int LN = LOADS == kE8 ? 10 : LOADS == kE16 ? 2 : LOADS == kO8 ? 8 : 16;
+  constexpr int L0 = LOADS == kE8 ? 8 : LOADS == kE10 ? 10 : 0;
+  constexpr int LN = LOADS == kE8 ? 10 : LOADS == kE10 ? 8 : LOADS == kO8 ? 8 : 10;
 #define MX_MFMA(i, j) acc[i][j] = mma<kBf16>(cur.b[j], cur.a[i], acc[i][j], xb[j], xa[i]);
 #define MX_FENCE __builtin_amdgcn_sched_barrier(0);
-#define MX_L(t) if constexpr ((t) < LN) load_n<kBf16>(plan, L0 + (t));
+// odd steps: load t in MFMA slot t; even steps: load t in slot 3 (t / 2) + t % 2
+#define MX_L(t)                                                                                   \
+  if constexpr (ODD) {                                                                            \
+    if constexpr ((t) < LN) load_n<kBf16>(plan, L0 + (t));                                        \
+  } else if constexpr ((t) % 3 != 2 && 2 * ((t) / 3) + (t) % 3 < LN) {                           \
+    load_n<kBf16>(plan, L0 + 2 * ((t) / 3) + (t) % 3);                                            \
+  }
 #define MX_E(x) if constexpr (!ODD) { x; }
 #define MX_SE(x) if constexpr (!kBf16 && !ODD) { x; }
 #define MX_SO(x) if constexpr (!kBf16 && ODD) { x; }
@@ -925,20 +931,20 @@ __global__ void __launch_bounds__(kThreads) k_gemm(Problem p, const int32_t* __r
   ld.s += 2;
   loader_seek<kWgrad, kBf16>(ld, w);
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  // Loads per k line (18 per wave): the odd step of slot 0 issues 0..15 of
-  // its plan and the next even step 16, 17; the odd step of slot 1 issues
+  // Loads per k line (18 per wave): the odd step of slot 0 issues 0..9 of
+  // its plan and the next even step 10..17; the odd step of slot 1 issues
   // 0..7 only (it may end a tile, whose epilogue stages through its slot's
   // rows 128-255) and the next even step 8..17.  Tiles hold a multiple of 4
   // steps, so a tile always ends on the odd step of slot 1.
   do {
     k_step<0, false, kE8, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<0, true, kO16, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
-    k_step<1, false, kE16, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<0, true, kO10, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+    k_step<1, false, kE10, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
     k_step<1, true, kO8, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
     while (c.s < c.t.steps) {
       k_step<0, false, kE8, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<0, true, kO16, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
-      k_step<1, false, kE16, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<0, true, kO10, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
+      k_step<1, false, kE10, kWgrad, kBf16>(st0, st1, fa, fb, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
       k_step<1, true, kO8, kWgrad, kBf16>(st0, st1, fb, fa, acc, ld, plan, ll, c, w, wm, wn, pa, pb, fo);
     }
   } while (finish_tile<kF32, kWgrad, kBf16>(c, w, acc, wm, wn, st1 + kEpiOff));
