@@ -385,11 +385,6 @@ struct Walk {
   __device__ __forceinline__ Coord at(int64_t L) const { return coord<kWgrad, kBf16>(p, sc, E, m_tiles, n_tiles, L); }
 };
 
-// Per-lane constants of the loads.  Code loads: lane l of wave w writes 16 B
-// of LDS block 4w + i (16 rows x 64 B): block row 16(4w + i) + l/4, LDS slot
-// l & 3, holding the global chunk (l & 3) ^ swz(row).  Scale loads: lane l
-// of wave w fetches the dword of tile row 64w + l.
-
 // Per-lane constants of the loads.  Code load i (0..7) of wave w covers 8
 // rows x 128 bytes: tile rows 128 (i >> 2) + 8 (4 (i & 3) + w) + l / 8, LDS
 // chunk l & 7 holding the global chunk (l & 7) ^ swz8(row).  The chunk is
@@ -453,11 +448,12 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
   return (uint32_t)(uintptr_t)(const lds_void*)p;
 }
 
-// The loads of one k line into one LDS slot: 18 instructions per wave.
-// Loads 0..7 (rows 0-127 of A and B: A0 B0 A1 B1 A2 B2 A3 B3) are issued in
-// the second half of an odd step, loads 8..15 (rows 128-255) and 16, 17 (the
-// A and B scale dwords) in the next even step.  A loader past its last tile
-// issues the same instructions with out-of-range offsets (they read zeros).
+// The loads of one k line into one LDS slot: 18 instructions per wave, in
+// this order: 0..7 rows 0-127 of A and B (A0 B0 A1 B1 A2 B2 A3 B3), 8..15
+// rows 128-255 (A4 B4 .. A7 B7), 16 and 17 the A and B scale dwords.  An odd
+// step issues the first 8 or 10 of them, the next even step the rest (see
+// k_step).  A loader past its last tile issues the same instructions with
+// out-of-range offsets (they read zeros).
 struct LoadPlan {
   v4u aq, bq, as, bs;
   uint32_t v[8];       // code voffsets (out of range where the lane's chunk is outside [k_lo, k_hi))
@@ -729,7 +725,8 @@ __device__ __forceinline__ void stage_barrier() {
 // eight fragments of the odd step (same slot, other k half) during the
 // second half.  Odd step: everything is in registers; a barrier at the start
 // frees the slot (every wave has read it), the loads of the k line after
-// next go into it from slot 0, the mid-step wait (vmcnt(8): those loads may
+// next go into it from the step's first MFMA slot, the mid-step wait
+// (vmcnt(8): the 8 loads issued before it may
 // still be in flight) and barrier make the next k line visible, and the
 // second half reads the next even step's fragments from the other slot.
 // LOADS: which loads of the current plan the step issues: even steps 8..17
