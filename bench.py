@@ -11,9 +11,10 @@ order, grouped GEMM wgrad; GEMM outputs in bf16.  Inputs are resident in HBM
 before the timed region.
 
 Printed: one JSON line.  ``value`` = GEMM FLOPs of a step (3 x 2*M*N*K over
-the real routed rows) / step time (the timed region over ``--steps`` steps),
-in TFLOP/s.  ``stages`` gives each stage's median duration (HIP events on
-the launch stream, every timed step; 70 steps, about 0.2 s, by default) and
+the real routed rows) / step time (the timed region over ``--steps`` eager
+steps, with no instrumentation inside it), in TFLOP/s.  ``stages`` gives
+each stage's median duration (HIP events around every stage, in a second
+pass of ``--steps`` steps; 70 steps, about 0.2 s each, by default) and
 its throughput against the MI355X peak (``frac``: MXFP8 dense 5.0 PFLOP/s,
 HBM 8 TB/s) and against the ceilings measured at the start of the run
 (``frac_ceiling``; ``ceilings``: a streaming copy and a scaled-MFMA-only
@@ -113,8 +114,12 @@ def ensure_built():
 
 def time_stages(run, names, steps, warmup, flush=None, label=""):
     """Run ``run(name)`` for every name, ``warmup`` untimed then ``steps`` timed
-    passes; per-stage HIP events on torch's current stream (the launch stream).
-    Returns (timed-region ms per pass, per-stage median ms, wall seconds).
+    passes with per-stage HIP events on torch's current stream (the launch
+    stream), for the per-stage medians; then (without ``flush``) ``steps``
+    more passes with no events inside the timed region, for the time per
+    pass, so that the event records between stages do not count in it.
+    Returns (ms per pass, per-stage median ms, wall seconds of the pass
+    whose time is returned).
     With ``flush`` (a callable), it runs before every stage, outside the
     stage's events (and inside the timed region).  In the counter pass each
     stage instead runs COUNTER_REPS times between markers labelled
@@ -157,6 +162,17 @@ def time_stages(run, names, steps, warmup, flush=None, label=""):
     total_ms = t_start.elapsed_time(t_end)
     per = {n: statistics.median(ev[i][j][0].elapsed_time(ev[i][j][1]) for i in range(steps))
            for j, n in enumerate(names)}
+    if flush is None:
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record()
+        for i in range(steps):
+            for n in names:
+                run(n)
+        t_end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        total_ms = t_start.elapsed_time(t_end)
     return total_ms / steps, per, wall
 
 
