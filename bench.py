@@ -18,7 +18,9 @@ pass of ``--steps`` steps; 70 steps, about 0.2 s each, by default) and
 its throughput against the MI355X peak (``frac``: MXFP8 dense 5.0 PFLOP/s,
 HBM 8 TB/s) and against the ceilings measured at the start of the run
 (``frac_ceiling``; ``ceilings``: a streaming copy and a scaled-MFMA-only
-loop, kernels of the library).  ``stages_mall_flushed`` times every stage
+loop, kernels of the library; the row+col quantize stages also carry
+``frac_pattern``, against the tile quantizer's loads and stores timed with
+no arithmetic).  ``stages_mall_flushed`` times every stage
 again after a 512 MB fill that evicts the Infinity Cache.
 ``small_configs`` times the tiny (forward, microseconds) and mid (forward +
 dgrad + wgrad) workloads.
@@ -191,11 +193,14 @@ def mall_flusher(nbytes=512 << 20):
 
 
 def measure_ceilings(copy_bytes=1344 << 20, reps=7):
-    """Measured ceilings of this part (library kernels mx_ceiling_copy and
-    mx_ceiling_mfma): the median HBM rate of a streaming copy of
-    ``copy_bytes`` (read + write bytes per second; 2.7 GB moved, the size of
-    the fused quantize's traffic) and the median rate of a loop of scaled
-    FP8 MFMAs in the grouped GEMMs' register pattern, on random operands (the
+    """Measured ceilings of this part (library kernels mx_ceiling_copy,
+    mx_ceiling_tile_pattern and mx_ceiling_mfma): the median HBM rate of a
+    streaming copy of ``copy_bytes`` (read + write bytes per second; 2.7 GB
+    moved, the size of the fused quantize's traffic), the median rate of the
+    tile quantizer's access pattern without its arithmetic on the
+    quantize-bandwidth tensor [131072, 5120] (bf16 in, both code
+    orientations out: 2.7 GB), and the median rate of a loop of scaled FP8
+    MFMAs in the grouped GEMMs' register pattern, on random operands (the
     rate the part sustains on real data: their switching power lowers the
     clock) and on near-constant operands (TFLOP/s)."""
     import statistics
@@ -209,30 +214,41 @@ def measure_ceilings(copy_bytes=1344 << 20, reps=7):
     wgs = dev.multi_processor_count
     out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda:0")
     iters = 20000
+    # the tile pattern reads [R, C] bf16 from the copy's source and writes both
+    # R x C code arrays into its destination (2 R C <= copy_bytes)
+    R, C = 131072, 5120
+    row_out, col_out = dst[:R * C], dst[R * C:2 * R * C]
     mxa.mx_ceiling_copy(src, dst, copy_bytes)
+    mxa.mx_ceiling_tile_pattern(src, row_out, col_out, R, C)
     mxa.mx_ceiling_mfma(out, wgs, 100, True)
     torch.cuda.synchronize()
-    cp, mf, mc = [], [], []
+    cp, tp, mf, mc = [], [], [], []
     for _ in range(reps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
         e[0].record()
         mxa.mx_ceiling_copy(src, dst, copy_bytes)
         e[1].record()
-        mxa.mx_ceiling_mfma(out, wgs, iters, True)
+        mxa.mx_ceiling_tile_pattern(src, row_out, col_out, R, C)
         e[2].record()
-        mxa.mx_ceiling_mfma(out, wgs, iters, False)
+        mxa.mx_ceiling_mfma(out, wgs, iters, True)
         e[3].record()
+        mxa.mx_ceiling_mfma(out, wgs, iters, False)
+        e[4].record()
         torch.cuda.synchronize()
         cp.append(e[0].elapsed_time(e[1]))
-        mf.append(e[1].elapsed_time(e[2]))
-        mc.append(e[2].elapsed_time(e[3]))
+        tp.append(e[1].elapsed_time(e[2]))
+        mf.append(e[2].elapsed_time(e[3]))
+        mc.append(e[3].elapsed_time(e[4]))
     flops = wgs * 4 * iters * 16 * 131072.0
     res = {"hbm_copy_gbps": round(2 * copy_bytes / (statistics.median(cp) * 1e-3) / 1e9, 1),
+           "quant_pattern_gbps": round(4 * R * C / (statistics.median(tp) * 1e-3) / 1e9, 1),
            "mfma_mxfp8_tflops": round(flops / (statistics.median(mf) * 1e-3) / 1e12, 1),
            "mfma_mxfp8_tflops_constant_operands": round(flops / (statistics.median(mc) * 1e-3) / 1e12, 1),
            "copy_bytes_moved": 2 * copy_bytes, "cus": wgs,
-           "note": "medians of 7 launches: mx_ceiling_copy (16-byte non-temporal streaming copy, read + write "
-                   "bytes / time) and mx_ceiling_mfma (16 independent 32x32x64 scaled FP8 MFMAs per wave on the GEMM "
+           "note": "medians of 7 launches: mx_ceiling_copy (16-byte non-temporal streaming copy, one chunk per "
+                   "thread, read + write bytes / time), mx_ceiling_tile_pattern (the row+col tile quantizer's loads "
+                   "and stores with no arithmetic, [131072, 5120] bf16 in, 4 bytes per element moved) and "
+                   "mx_ceiling_mfma (16 independent 32x32x64 scaled FP8 MFMAs per wave on the GEMM "
                    "step's 4 A + 4 B register fragments, one wave per SIMD); mfma_mxfp8_tflops uses random codes "
                    "and scales (the ceiling on real data), the constant-operand figure shows the clock headroom "
                    "that data-dependent power takes away"}
@@ -260,6 +276,11 @@ def time_graph(g, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+# stages that quantize a plain bf16 tensor in both orientations: their
+# frac_pattern compares them with the tile quantizer's own access pattern
+ROWCOL_QUANT_STAGES = ("quant_w", "quant_dy")
+
+
 def stage_entry(n, ms, work, ceil):
     """Throughput of one stage against the published peak (frac) and the
     measured ceiling (frac_ceiling)."""
@@ -268,8 +289,11 @@ def stage_entry(n, ms, work, ceil):
         return {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_MXFP8_TFLOPS, 4),
                 "frac_ceiling": round(tf / ceil["mfma_mxfp8_tflops"], 4)}
     gbs = work["bytes"][n] / (ms * 1e-3) / 1e9
-    return {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
-            "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4)}
+    e = {"ms": round(ms, 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
+         "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4)}
+    if n in ROWCOL_QUANT_STAGES:
+        e["frac_pattern"] = round(gbs / ceil["quant_pattern_gbps"], 4)
+    return e
 
 
 def gpu_expert_path(args, c, ceil):
@@ -482,6 +506,8 @@ def gpu_quantize_bandwidth(args, ceil):
         tr = measured_traffic("quant." + n)
         out[n] = {"ms": round(per[n], 4), "gbps": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBPS, 4),
                   "frac_ceiling": round(gbs / ceil["hbm_copy_gbps"], 4), "traffic": None if tr is None else tr["bytes"]}
+        if n == "quant_rowcol":
+            out[n]["frac_pattern"] = round(gbs / ceil["quant_pattern_gbps"], 4)
     counter_work("quant.", nbytes)
     out["shape"] = [rows, cols]
     del x, q, s, qt, st, y, yt
@@ -903,7 +929,8 @@ def main():
         import torch
         global COUNTER
         COUNTER = {"labels": [], "alg": {}, "marker": torch.empty(1, dtype=torch.int64, device="cuda:0")}
-        ceil = {"hbm_copy_gbps": 1.0, "mfma_mxfp8_tflops": 1.0, "mfma_mxfp8_tflops_constant_operands": 1.0}
+        ceil = {"hbm_copy_gbps": 1.0, "quant_pattern_gbps": 1.0, "mfma_mxfp8_tflops": 1.0,
+                "mfma_mxfp8_tflops_constant_operands": 1.0}
     else:
         ceil = measure_ceilings()
     res = gpu_expert_path(args, c, ceil)

@@ -334,10 +334,18 @@ int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const in
  * benchmark reports its roofline fractions against, next to the published
  * peaks.
  *
- * mx_ceiling_copy: a streaming copy of `bytes` (a multiple of 16384; src
+ * mx_ceiling_copy: a streaming copy of `bytes` (a multiple of 4096; src
  *   and dst 16-byte aligned device buffers that do not overlap), 16-byte
- *   non-temporal loads and stores -- the HBM read + write rate an HBM-bound
- *   kernel can reach.
+ *   non-temporal loads and stores, one per thread -- the HBM read + write
+ *   rate an HBM-bound kernel can reach.
+ * mx_ceiling_tile_pattern: the memory traffic of a quantize that writes
+ *   both orientations, without its arithmetic: x [rows, cols] bf16 is read
+ *   in 128 x 128 tiles as the tile quantizer reads it, and each tile is
+ *   written as 1 byte per element to row_out [rows, cols] (row-major, 128
+ *   bytes per tile row) and to col_out [cols, rows] (column-major, 128
+ *   bytes per tile column); 4 * rows * cols bytes moved, the fused row+col
+ *   quantize's traffic minus its scale bytes.  rows and cols multiples of
+ *   128; the three device buffers 16-byte aligned and not overlapping.
  * mx_ceiling_mfma: `workgroups` workgroups of 256 threads, each wave running
  *   `iters` rounds of 16 independent V_MFMA_SCALE_F32_32X32X64_F8F6F4 on
  *   register operands in the grouped GEMM's register pattern (4 A and 4 B
@@ -348,6 +356,8 @@ int mx_bf16_grouped_gemm_wgrad(const uint16_t* dyt, const uint16_t* xt, const in
  *   float per thread to out [workgroups * 256].
  */
 int mx_ceiling_copy(const void* src, void* dst, int64_t bytes, mx_stream_t stream);
+int mx_ceiling_tile_pattern(const void* x, void* row_out, void* col_out, int64_t rows, int64_t cols,
+                            mx_stream_t stream);
 int mx_ceiling_mfma(float* out, int32_t workgroups, int32_t iters, int32_t random_operands, mx_stream_t stream);
 
 #ifdef __cplusplus

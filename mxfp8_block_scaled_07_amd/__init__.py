@@ -30,6 +30,7 @@ _SIGNATURES = {
     "mx_permute": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "mx_permute_noalloc": (ctypes.c_int, [_vp, _vp, _i64, _i64, _vp, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mx_ceiling_copy": (ctypes.c_int, [_vp, _vp, _i64, _vp]),
+    "mx_ceiling_tile_pattern": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _vp]),
     "mx_ceiling_mfma": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp]),
     "mx_grouped_gemm_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
     "mx_grouped_gemm_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _vp, _i32, _vp]),
@@ -112,6 +113,11 @@ def mx_permute_noalloc(q, s, tokens, cols, expert_ids, topk, num_experts, capaci
 
 def mx_ceiling_copy(src, dst, nbytes, stream=None):
     _check(lib().mx_ceiling_copy(_p(src), _p(dst), nbytes, _s(stream)), "mx_ceiling_copy")
+
+
+def mx_ceiling_tile_pattern(x, row_out, col_out, rows, cols, stream=None):
+    _check(lib().mx_ceiling_tile_pattern(_p(x), _p(row_out), _p(col_out), rows, cols, _s(stream)),
+           "mx_ceiling_tile_pattern")
 
 
 def mx_ceiling_mfma(out, workgroups, iters, random_operands=True, stream=None):

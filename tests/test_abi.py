@@ -232,3 +232,19 @@ def test_permute_noalloc_validation(lib):
     T, E = 1 << 18, 16384
     assert lib.mx_permute_workspace_size(T, 1, E) > (4 << 20)
     assert p(None, None, T, 0, P, 1, E, T + 31 * E, None, None, P, P, P, None) == mxa.MX_EUNSUPPORTED
+
+
+def test_ceiling_validation(lib):
+    c = lib.mx_ceiling_copy
+    assert c(None, P, 4096, None) == mxa.MX_EINVAL                                 # src null
+    assert c(P, P, 4096 + 16, None) == mxa.MX_EINVAL                               # bytes % 4096
+    assert c(P, P, 0, None) == mxa.MX_EINVAL                                       # empty
+    assert c(Q, P, 4096, None) == mxa.MX_EINVAL                                    # src not 16-aligned
+    m = lib.mx_ceiling_mfma
+    assert m(None, 1, 1, 1, None) == mxa.MX_EINVAL                                 # out null
+    assert m(P, 0, 1, 1, None) == mxa.MX_EINVAL                                    # no workgroups
+    t = lib.mx_ceiling_tile_pattern
+    assert t(None, P, P, 128, 128, None) == mxa.MX_EINVAL                          # x null
+    assert t(P, P, P, 96, 128, None) == mxa.MX_EINVAL                              # rows % 128
+    assert t(P, P, P, 128, 160, None) == mxa.MX_EINVAL                             # cols % 128
+    assert t(P, Q, P, 128, 128, None) == mxa.MX_EINVAL                             # row_out not 16-aligned
