@@ -149,13 +149,19 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
   }
 }
 
-// One wave per output row; 4 rows per block.  Rows copy codes then scales.
 // Token-major copy: block t < tokens reads token t's code row and scale
 // dwords once and writes them to its topk rows dst_row[t*topk + j] (ids out
 // of range have dst -1 and are skipped), so each source byte is read once
-// however many experts the token goes to.  Blocks past the tokens zero the
-// pad rows (src_row < 0), four rows per block.  Every output row is written
-// by exactly one block.
+// however many experts the token goes to.  Up to kDirectK destinations are
+// read with uniform loads that are in flight together with the first code
+// loads; larger topk stage them through LDS in chunks of kMaxK.  Blocks past
+// the tokens zero the pad rows (src_row < 0): each wave checks kPadRows
+// consecutive rows with one ballot and zeroes the pad rows among them
+// (rows past the last group are all pad, so few rows per wave keep that
+// work spread).  Every output row is written by exactly one block.
+constexpr int kDirectK = 8;
+constexpr int kPadRows = 4;
+
 __global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                                         int64_t tokens, int64_t cols, int32_t topk,
                                                         const int32_t* __restrict__ dst_row,
@@ -171,7 +177,31 @@ __global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restric
   if (blk < tokens) {
     const int64_t t = blk;
     const uint4* qs = reinterpret_cast<const uint4*>(q + t * cols);
-    // slots in chunks of kMaxK (one chunk for every topk up to 64)
+    if (topk <= kDirectK) {
+      int32_t d[kDirectK];
+#pragma unroll
+      for (int j = 0; j < kDirectK; ++j) {
+        d[j] = -1;
+        if (j < topk) {
+          const int32_t x = dst_row[t * topk + j];
+          d[j] = x >= 0 && x < capacity ? x : -1;
+        }
+      }
+      for (int64_t i = threadIdx.x; i < nq; i += blockDim.x) {
+        const uint4 v = qs[i];
+#pragma unroll
+        for (int j = 0; j < kDirectK; ++j)
+          if (d[j] >= 0) reinterpret_cast<uint4*>(q_out + (int64_t)d[j] * cols)[i] = v;
+      }
+      for (int64_t p = threadIdx.x; p < np; p += blockDim.x) {
+        const uint32_t v = ss[p * tokens + t];
+#pragma unroll
+        for (int j = 0; j < kDirectK; ++j)
+          if (d[j] >= 0) sd[p * capacity + d[j]] = v;
+      }
+      return;
+    }
+    // slots in chunks of kMaxK
     for (int32_t j0 = 0; j0 < topk; j0 += kMaxK) {
       const int32_t nk = topk - j0 < kMaxK ? topk - j0 : kMaxK;
       __syncthreads();  // the previous chunk's readers are done with dl
@@ -197,14 +227,20 @@ __global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restric
     }
     return;
   }
-  const int64_t r = (blk - tokens) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (r >= capacity) return;
-  const int32_t src = src_row[r];
-  if (src >= 0 && src < tokens) return;
-  uint4* qd = reinterpret_cast<uint4*>(q_out + r * cols);
-  for (int64_t i = lane; i < nq; i += 64) qd[i] = make_uint4(0, 0, 0, 0);
-  for (int64_t p = lane; p < np; p += 64) sd[p * capacity + r] = 0u;
+  const int64_t r0 = ((blk - tokens) * 4 + (threadIdx.x >> 6)) * kPadRows;
+  if (r0 >= capacity) return;
+  bool pad = false;
+  if (lane < kPadRows && r0 + lane < capacity) {
+    const int32_t src = src_row[r0 + lane];
+    pad = !(src >= 0 && src < tokens);
+  }
+  for (uint64_t m = __ballot(pad); m != 0; m &= m - 1) {
+    const int64_t r = r0 + __builtin_ctzll(m);
+    uint4* qd = reinterpret_cast<uint4*>(q_out + r * cols);
+    for (int64_t i = lane; i < nq; i += 64) qd[i] = make_uint4(0, 0, 0, 0);
+    for (int64_t p = lane; p < np; p += 64) sd[p * capacity + r] = 0u;
+  }
 }
 
 }  // namespace
@@ -239,7 +275,8 @@ static int permute_check(const uint8_t* q, const uint8_t* s, int64_t tokens, int
   const int64_t n = tokens * topk;
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
   if (route_tiles(n, num_experts) > 0x7FFFFFFF) return MX_EINVAL;
-  if (copy && tokens + (capacity_rows + 3) / 4 > 0x7FFFFFFF) return MX_EINVAL;  // k_permute_tokens grid
+  if (copy && tokens + (capacity_rows + 4 * kPadRows - 1) / (4 * kPadRows) > 0x7FFFFFFF)
+    return MX_EINVAL;  // k_permute_tokens grid
   return MX_OK;
 }
 
@@ -253,7 +290,7 @@ static int permute_launch(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   const int64_t n = tokens * topk;
   const int32_t tile = route_tile(num_experts);
   const int64_t nt = route_tiles(n, num_experts) > 0 ? route_tiles(n, num_experts) : 1;
-  const int64_t copy_blocks = tokens + (capacity_rows + 3) / 4;
+  const int64_t copy_blocks = tokens + (capacity_rows + 4 * kPadRows - 1) / (4 * kPadRows);
   int32_t* hist = workspace;
   int32_t* base = hist + nt * num_experts;
   const size_t lds = (size_t)num_experts * sizeof(int32_t);  // <= 64 KB (kMaxExperts)

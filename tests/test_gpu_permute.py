@@ -62,11 +62,44 @@ def test_top8_of_64_routing():
 
 @pytest.mark.parametrize("T,topk,E", [(1, 1, 1), (5, 3, 2), (63, 2, 7), (4097, 1, 3), (3000, 2, 300), (100, 4, 1),
                                       (5000, 2, 2048),      # above 1024 experts: 4096-pair routing tiles
-                                      (3000, 1, 16384)])    # the largest expert count (most experts empty)
+                                      (3000, 1, 16384),     # the largest expert count (most experts empty)
+                                      (300, 8, 16),         # the most destinations the copy reads directly
+                                      (250, 9, 16)])        # one more: destinations staged through LDS
 def test_edge_shapes(T, topk, E):
     g = np.random.default_rng(T * 7 + E)
     ids = g.integers(0, E, (T, topk))
     check_permute(ids, E, K=32 * int(g.integers(1, 4)), seed=T)
+
+
+@pytest.mark.parametrize("T,topk,E", [(300, 3, 7), (20000, 2, 9), (2000, 12, 600)])
+def test_out_of_range_ids_are_ignored(T, topk, E):
+    """Pairs whose expert id is negative or >= E get dst_row -1, count in no
+    group and are not copied; the valid pairs keep their flat-order ranks.
+    Expected values: the oracle's routing with one extra expert E that
+    collects the invalid pairs (it sorts after every real expert, so experts
+    0..E-1 get the same offsets and rows as with those pairs dropped)."""
+    g = np.random.default_rng(T + E)
+    ids = g.integers(0, E, (T, topk)).astype(np.int32)
+    flat = ids.reshape(-1)
+    flat[::29] = -1
+    flat[7::41] = E + 5
+    bad = (flat < 0) | (flat >= E)
+    cap = T * topk + 31 * E
+    _, off, dst, src = routing.route(np.where(bad, E, flat).reshape(T, topk), E + 1, cap + 31)
+    off = off[:E + 1]
+    dst = np.where(bad, -1, dst)
+    src = src[:cap].copy()
+    src[off[E]:] = -1
+    K = 64
+    xb = workloads.normal_bf16(g, (T, K))
+    q, s = mx.quantize_rowwise(xb)
+    q_out, s_out, goff, gdst, gsrc = mxa.permute(dev(q), dev(spanels(s)), dev(ids), E, cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(goff), off)
+    assert np.array_equal(host(gdst), dst)
+    assert np.array_equal(host(gsrc), src)
+    oq, os_ = routing.permute(q, s, src)
+    assert np.array_equal(host(q_out), oq) and np.array_equal(srows(s_out, K), os_)
 
 
 def test_all_tokens_one_expert_and_duplicates():
