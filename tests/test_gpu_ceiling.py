@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import mxfp8_block_scaled_07_amd as mxa
+from ceiling_ref import tile_pattern_expected
 
 pytestmark = pytest.mark.gpu
 
@@ -33,28 +34,6 @@ def test_ceiling_mfma_writes_finite_sums():
         assert bool(torch.isfinite(out).all())
 
 
-def _tile_pattern_expected(x32, rows, cols):
-    """Both outputs of the tile-pattern helper from its documented thread
-    map, on x viewed as uint32 [rows, cols / 2] (4 words per 16-byte chunk)."""
-    row = np.empty((rows, cols // 4), np.uint32)
-    row[:, 0::2] = x32[:, 0::4] ^ x32[:, 1::4]
-    row[:, 1::2] = x32[:, 2::4] ^ x32[:, 3::4]
-    col = np.empty((cols, rows // 4), np.uint32)
-    t = np.arange(256)
-    w, lane = t >> 6, t & 63
-    ch, ry = lane & 15, lane >> 4
-    for tr in range(rows // 128):
-        for tc in range(cols // 128):
-            r0 = tr * 128 + 32 * w + 8 * ry
-            for s in range(4):
-                q = 256 * s + t
-                words = (tc * 128 + 8 * ch) // 2 + np.arange(4)[:, None]          # [4, 256]
-                v = x32[r0 + 2 * s, words] ^ x32[r0 + 2 * s + 1, words]
-                dst = tr * 32 + 4 * (q & 7) + np.arange(4)[:, None]
-                col[tc * 128 + (q >> 3), dst] = v
-    return row, col
-
-
 @pytest.mark.parametrize("rows,cols", [(128, 128), (256, 384), (384, 256)])
 def test_ceiling_tile_pattern_moves_the_documented_bytes(rows, cols):
     g = torch.Generator(device="cuda:0")
@@ -64,7 +43,7 @@ def test_ceiling_tile_pattern_moves_the_documented_bytes(rows, cols):
     col_out = torch.full((rows * cols + 4096,), 0xA5, dtype=torch.uint8, device="cuda:0")
     mxa.mx_ceiling_tile_pattern(x, row_out, col_out, rows, cols)
     torch.cuda.synchronize()
-    row, col = _tile_pattern_expected(x.cpu().numpy().view(np.uint32), rows, cols)
+    row, col = tile_pattern_expected(x.cpu().numpy().view(np.uint32), rows, cols)
     assert np.array_equal(row_out[:rows * cols].cpu().numpy().view(np.uint32).reshape(rows, cols // 4), row)
     assert np.array_equal(col_out[:rows * cols].cpu().numpy().view(np.uint32).reshape(cols, rows // 4), col)
     for buf in (row_out, col_out):
