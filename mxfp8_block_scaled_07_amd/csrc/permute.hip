@@ -9,8 +9,9 @@
 // Deterministic, stable ranks without ordering atomics:
 //   1. k_route_hist   per routing tile (512 flat pairs; 4096 above 1024
 //                     experts), an expert histogram
-//   2. k_route_scan   counts, padded exclusive scan -> group_offsets, and the
-//                     first row of every (tile, expert)
+//   2. k_route_scan   counts, padded exclusive scan -> group_offsets, the
+//                     first row of every (tile, expert), and src_row -1 for
+//                     the pad rows and the rows past the last group
 //   3. k_route_rank   one wave per tile walks its pairs in flat order; a pair's
 //                     row is its tile base + the number of earlier pairs of the
 //                     same expert (wave ballots give the in-chunk part)
@@ -53,11 +54,15 @@ __global__ void __launch_bounds__(256) k_route_hist(const int32_t* __restrict__ 
 // thread sums (then prefix-sums) its group's tiles for its expert.  Pass 1
 // gives every expert's count; the padded exclusive scan over experts gives
 // group_offsets; pass 2 writes, for every (tile, expert), the first row of
-// that tile's pairs of that expert.
+// that tile's pairs of that expert, and marks the rows no pair will take
+// (each group's pad rows and the rows past the last group) with src_row -1.
+// k_route_rank writes every other src_row entry: each is written once.
 __global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__ hist, int32_t ntiles, int32_t E,
-                                                     int32_t* __restrict__ base, int32_t* __restrict__ offsets) {
+                                                     int32_t* __restrict__ base, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ src_row, int64_t capacity) {
   extern __shared__ int32_t padded[];       // E entries
   __shared__ int32_t part[32][33];          // [expert in chunk][tile group]
+  __shared__ int32_t used;                  // rows of all groups, padding included
   const int le = threadIdx.x & 31, grp = threadIdx.x >> 5;
   const int32_t per = (ntiles + 31) / 32;
   const int32_t t0 = grp * per, t1 = t0 + per < ntiles ? t0 + per : ntiles;
@@ -84,8 +89,10 @@ __global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__
       acc += p;
     }
     offsets[E] = acc;
+    used = acc;
   }
   __syncthreads();
+  for (int64_t r = used + threadIdx.x; r < capacity; r += blockDim.x) src_row[r] = -1;
   for (int32_t e0 = 0; e0 < E; e0 += 32) {
     const int32_t e = e0 + le;
     int32_t c = 0;
@@ -99,6 +106,10 @@ __global__ void __launch_bounds__(1024) k_route_scan(const int32_t* __restrict__
       for (int32_t t = t0; t < t1; ++t) {
         base[(int64_t)t * E + e] = acc;
         acc += hist[(int64_t)t * E + e];
+      }
+      if (grp == 31) {  // acc is now the group's first pad row
+        const int32_t end = e + 1 < E ? padded[e + 1] : used;
+        for (int32_t r = acc; r < end; ++r) src_row[r] = -1;
       }
     }
     __syncthreads();
@@ -300,10 +311,7 @@ static int permute_launch(const uint8_t* q, const uint8_t* s, int64_t tokens, in
     hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, st, hist, (int64_t)num_experts, 0);
   }
   hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(1024), lds, st, hist, (int32_t)nt, num_experts, base,
-                     group_offsets);
-  const int64_t fill_blocks = (capacity_rows + 255) / 256 < 65536 ? (capacity_rows + 255) / 256 : 65536;
-  if (capacity_rows > 0)
-    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)fill_blocks), dim3(256), 0, st, src_row, capacity_rows, -1);
+                     group_offsets, src_row, capacity_rows);
   if (n > 0)
     hipLaunchKernelGGL(k_route_rank, dim3((unsigned)nt), dim3(64), lds, st, expert_ids, n, topk, num_experts, tile,
                        base, dst_row, src_row, capacity_rows);

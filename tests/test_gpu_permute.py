@@ -102,6 +102,23 @@ def test_out_of_range_ids_are_ignored(T, topk, E):
     assert np.array_equal(host(q_out), oq) and np.array_equal(srows(s_out, K), os_)
 
 
+def test_no_tokens():
+    """A call with no tokens: every group is empty, every row of the
+    capacity is a pad row (src_row -1, zero codes and scales)."""
+    E, K, cap = 4, 64, 4 * 31 + 40
+    ids = torch.zeros((0, 2), dtype=torch.int32, device="cuda:0")
+    # one-row sources: with no tokens nothing is read from them (an empty
+    # tensor may have a null data pointer, which the copy rejects)
+    q = torch.zeros((1, K), dtype=torch.uint8, device="cuda:0")
+    s = torch.zeros(mxa.scale_shape(1, K), dtype=torch.uint8, device="cuda:0")
+    q_out, s_out, goff, gdst, gsrc = mxa.permute(q, s, ids, E, cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(goff), np.zeros(E + 1))
+    assert host(gdst).size == 0
+    assert np.array_equal(host(gsrc), np.full(cap, -1))
+    assert not host(q_out).any() and not host(s_out).any()
+
+
 def test_all_tokens_one_expert_and_duplicates():
     ids = np.zeros((300, 2), np.int32)
     ids[::3, 1] = 2
