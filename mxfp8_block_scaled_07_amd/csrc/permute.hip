@@ -163,7 +163,9 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
 // Token-major copy: block t < tokens reads token t's code row and scale
 // dwords once and writes them to its topk rows dst_row[t*topk + j] (ids out
 // of range have dst -1 and are skipped), so each source byte is read once
-// however many experts the token goes to.  Up to kDirectK destinations are
+// however many experts the token goes to.  The block has one thread per
+// 16-byte chunk of a row (rounded up to whole waves, at most 1024), so
+// every thread moves one chunk of rows up to 16 KB.  Up to kDirectK destinations are
 // read with uniform loads that are in flight together with the first code
 // loads; larger topk stage them through LDS in chunks of kMaxK.  Blocks past
 // the tokens zero the pad rows (src_row < 0): each wave checks kPadRows
@@ -173,7 +175,20 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
 constexpr int kDirectK = 8;
 constexpr int kPadRows = 4;
 
-__global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
+// Threads per block of k_permute_tokens for rows of `cols` codes.
+inline int copy_threads(int64_t cols) {
+  const int64_t nq = cols >> 4;
+  return nq >= 1024 ? 1024 : nq <= 64 ? 64 : (int)((nq + 63) & ~int64_t(63));
+}
+
+// Its grid: one block per token, then blocks of (threads / 64) waves of
+// kPadRows rows over the capacity.
+inline int64_t copy_grid(int64_t tokens, int64_t capacity, int64_t cols) {
+  const int64_t rows_per_block = (int64_t)(copy_threads(cols) / 64) * kPadRows;
+  return tokens + (capacity + rows_per_block - 1) / rows_per_block;
+}
+
+__global__ void __launch_bounds__(1024) k_permute_tokens(const uint8_t* __restrict__ q, const uint8_t* __restrict__ s,
                                                         int64_t tokens, int64_t cols, int32_t topk,
                                                         const int32_t* __restrict__ dst_row,
                                                         const int32_t* __restrict__ src_row, int64_t capacity,
@@ -239,7 +254,7 @@ __global__ void __launch_bounds__(256) k_permute_tokens(const uint8_t* __restric
     return;
   }
   const int lane = threadIdx.x & 63;
-  const int64_t r0 = ((blk - tokens) * 4 + (threadIdx.x >> 6)) * kPadRows;
+  const int64_t r0 = ((blk - tokens) * (int64_t)(blockDim.x >> 6) + (threadIdx.x >> 6)) * kPadRows;
   if (r0 >= capacity) return;
   bool pad = false;
   if (lane < kPadRows && r0 + lane < capacity) {
@@ -286,8 +301,7 @@ static int permute_check(const uint8_t* q, const uint8_t* s, int64_t tokens, int
   const int64_t n = tokens * topk;
   if (capacity_rows < n + 31 * (int64_t)num_experts || capacity_rows > 0x7FFFFFFF) return MX_EINVAL;
   if (route_tiles(n, num_experts) > 0x7FFFFFFF) return MX_EINVAL;
-  if (copy && tokens + (capacity_rows + 4 * kPadRows - 1) / (4 * kPadRows) > 0x7FFFFFFF)
-    return MX_EINVAL;  // k_permute_tokens grid
+  if (copy && copy_grid(tokens, capacity_rows, cols) > 0x7FFFFFFF) return MX_EINVAL;  // k_permute_tokens grid
   return MX_OK;
 }
 
@@ -301,7 +315,7 @@ static int permute_launch(const uint8_t* q, const uint8_t* s, int64_t tokens, in
   const int64_t n = tokens * topk;
   const int32_t tile = route_tile(num_experts);
   const int64_t nt = route_tiles(n, num_experts) > 0 ? route_tiles(n, num_experts) : 1;
-  const int64_t copy_blocks = tokens + (capacity_rows + 4 * kPadRows - 1) / (4 * kPadRows);
+  const int64_t copy_blocks = copy_grid(tokens, capacity_rows, cols);
   int32_t* hist = workspace;
   int32_t* base = hist + nt * num_experts;
   const size_t lds = (size_t)num_experts * sizeof(int32_t);  // <= 64 KB (kMaxExperts)
@@ -316,8 +330,8 @@ static int permute_launch(const uint8_t* q, const uint8_t* s, int64_t tokens, in
     hipLaunchKernelGGL(k_route_rank, dim3((unsigned)nt), dim3(64), lds, st, expert_ids, n, topk, num_experts, tile,
                        base, dst_row, src_row, capacity_rows);
   if (copy && capacity_rows > 0)
-    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)copy_blocks), dim3(256), 0, st, q, s, tokens, cols, topk,
-                       dst_row, src_row, capacity_rows, q_out, s_out);
+    hipLaunchKernelGGL(k_permute_tokens, dim3((unsigned)copy_blocks), dim3(copy_threads(cols)), 0, st, q, s, tokens,
+                       cols, topk, dst_row, src_row, capacity_rows, q_out, s_out);
   return launch_status();
 }
 
