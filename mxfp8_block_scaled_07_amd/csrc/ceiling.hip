@@ -20,8 +20,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 // loads and stores.  Of the patterns timed on this part (1, 2, 4 or 8
 // chunks per thread, default or non-temporal policy on either side, 256- or
 // 1024-thread blocks), one chunk per thread in 256-thread blocks with both
-// sides non-temporal is the fastest: small blocks spread consecutive 4 KB
-// pieces over all XCDs and every wave keeps one request in flight.
+// sides non-temporal is the fastest.
 __global__ void __launch_bounds__(256) k_copy(const v4u* __restrict__ src, v4u* __restrict__ dst) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
@@ -37,8 +36,7 @@ __global__ void __launch_bounds__(256) k_copy(const v4u* __restrict__ src, v4u* 
 // column, the columnwise codes' lines).  The values written are XORs of the
 // loaded ones, so every load is used.  Loads are non-temporal: of the
 // policies timed on this pattern that is the faster one (the quantizer
-// itself is faster with default loads, whose scheduling its arithmetic
-// hides).
+// itself measured faster with default loads).
 __global__ void __launch_bounds__(256) k_tile_pattern(const uint8_t* __restrict__ x, uint8_t* __restrict__ row_out,
                                                        uint8_t* __restrict__ col_out, int64_t rows, int64_t cols,
                                                        int32_t n_tc) {

@@ -164,14 +164,14 @@ __global__ void __launch_bounds__(64) k_route_rank(const int32_t* __restrict__ i
 // dwords once and writes them to its topk rows dst_row[t*topk + j] (ids out
 // of range have dst -1 and are skipped), so each source byte is read once
 // however many experts the token goes to.  The block has one thread per
-// 16-byte chunk of a row (rounded up to whole waves, at most 1024), so
-// every thread moves one chunk of rows up to 16 KB.  Up to kDirectK destinations are
-// read with uniform loads that are in flight together with the first code
-// loads; larger topk stage them through LDS in chunks of kMaxK.  Blocks past
-// the tokens zero the pad rows (src_row < 0): each wave checks kPadRows
-// consecutive rows with one ballot and zeroes the pad rows among them
-// (rows past the last group are all pad, so few rows per wave keep that
-// work spread).  Every output row is written by exactly one block.
+// 16-byte chunk of a row (rounded up to whole waves, at most 1024), so in
+// rows up to 16 KB every thread moves one chunk.  Up to kDirectK
+// destinations are read with uniform loads that are in flight together with
+// the first code loads; larger topk stage them through LDS in chunks of
+// kMaxK.  Blocks past the tokens zero the pad rows (src_row < 0): each wave
+// checks kPadRows consecutive rows with one ballot and zeroes the pad rows
+// among them (rows past the last group are all pad, so few rows per wave
+// keep that work spread).  Every output row is written by exactly one block.
 constexpr int kDirectK = 8;
 constexpr int kPadRows = 4;
 
