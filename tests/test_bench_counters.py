@@ -91,3 +91,17 @@ def test_traffic_record_ignored_when_sources_change(tmp_path, monkeypatch):
     assert bench.measured_traffic("gemm_fwd")["bytes"] == 15.0
     src.write_text("kernel v2")
     assert bench.measured_traffic("gemm_fwd") is None
+
+
+def test_stage_entry_fractions():
+    """A stage's throughput against the spec peak (frac), the measured copy or
+    MFMA-loop ceiling (frac_ceiling) and, for the row+col quantizes of plain
+    tensors, the tile quantizer's access pattern (frac_pattern)."""
+    work = {"gemm_flops": {"gemm_fwd": 2e12}, "bytes": {"quant_w": 4e9, "permute": 1e8}}
+    ceil = {"hbm_copy_gbps": 5000.0, "quant_pattern_gbps": 4000.0, "mfma_mxfp8_tflops": 2500.0}
+    e = bench.stage_entry("gemm_fwd", 1.0, work, ceil)           # 2e12 FLOP in 1 ms
+    assert e == {"ms": 1.0, "tflops": 2000.0, "frac": 0.4, "frac_ceiling": 0.8}
+    e = bench.stage_entry("quant_w", 1.0, work, ceil)            # 4e9 bytes in 1 ms
+    assert e == {"ms": 1.0, "gbps": 4000.0, "frac": 0.5, "frac_ceiling": 0.8, "frac_pattern": 1.0}
+    e = bench.stage_entry("permute", 2.0, work, ceil)
+    assert e == {"ms": 2.0, "gbps": 50.0, "frac": 0.0063, "frac_ceiling": 0.01}
