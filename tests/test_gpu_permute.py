@@ -119,6 +119,13 @@ def test_no_tokens():
     assert not host(q_out).any() and not host(s_out).any()
 
 
+def test_rows_wider_than_one_block():
+    """Rows of 16416 codes (1026 16-byte chunks, 129 scale panels): the copy's
+    1024-thread blocks loop over the chunks."""
+    g = np.random.default_rng(11)
+    check_permute(g.integers(0, 5, (70, 2)), 5, K=16416, seed=11)
+
+
 def test_all_tokens_one_expert_and_duplicates():
     ids = np.zeros((300, 2), np.int32)
     ids[::3, 1] = 2
